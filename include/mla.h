@@ -1,0 +1,196 @@
+/*
+ * mla.h -- C ABI of a gfx950 (MI355X) library for Multi-head Latent
+ * Attention (MLA) over a paged, compressed latent KV cache.
+ *
+ * Sources (web pages on the TokenSpeed inference engine):
+ *   [TALK] "构建面向 Agentic 推理的下一代 LLM 推理引擎" -- AICon 2026 Shenzhen
+ *          talk transcript.
+ *   [NEWS] "英偉達力薦，小團隊兩個月開源一款「光速級」智能體推理引擎" -- news
+ *          article on the TokenSpeed blog post.
+ *
+ * What is computed.  [TALK, section "Kernel：让 MLA 真正跑满 GPU"]: MLA keeps
+ * the KV of every head as one compressed latent row per token, and the first
+ * product of decode attention is query x latent key.  Here (absorbed form)
+ * a cache row is 576 bf16 values, the 512 latent columns followed by the 64
+ * rope columns; the key of a token is its whole row and its value is the
+ * first 512 columns of that same row; all query heads attend the same rows.
+ * For a query row q (576 values) of request b and the rows t it sees:
+ *
+ *     s_t  = softmax_scale * <q, row_t>
+ *     lse  = ln sum_t exp(s_t)                       (natural log, fp32)
+ *     out  = sum_t exp(s_t - lse) * row_t[0:512]     (bf16, rounded to nearest even)
+ *
+ * Causality: a request with L cached rows and n new query tokens (the last
+ * n of its L rows) lets new token i (0-based) see rows 0 .. L-n+i.  That
+ * covers speculative-decoding verification, where the drafts are causal
+ * among themselves [NEWS, section "TokenSpeed 性能預覽"], and prefill after
+ * a cached prefix, where Q and KV lengths differ [TALK, section
+ * "Kernel：让 MLA 真正跑满 GPU"].
+ *
+ * Memory layouts (all device memory, all row-major, no padding):
+ *   query      bf16 [tokens, num_heads, 576]
+ *   kv_cache   bf16 or int8 [num_pages, page_size, 576]; page_size must be 64
+ *   kv_scale   fp32 [num_pages, page_size]: per-row scale of the int8 cache
+ *              (row value = code * scale); NULL for a bf16 cache
+ *   page_table int32 [batch, max_pages_per_req]: physical page of logical
+ *              page j of request b; only entries j < ceil(L_b / 64) are read
+ *   out        bf16 [tokens, num_heads, 512]
+ *   lse        fp32 [tokens, num_heads]
+ *
+ * Ownership and streams.  The caller allocates every buffer; the library
+ * never allocates or frees device memory, never synchronises, keeps no
+ * pointer after a call returns, and enqueues all work on `hip_stream`
+ * (a hipStream_t; NULL is the default stream).  Buffers must stay valid
+ * until that work has finished.  The workspace is scratch owned by the call
+ * while it runs; calls that share one workspace must be ordered on one stream.
+ *
+ * Errors.  Every function returns an MLA_STATUS code.  Host-side scalar
+ * arguments are all checked before any HIP call, so invalid arguments are
+ * reported on a machine without a GPU.  Device-resident lengths are
+ * preconditions, not checked: q_len <= seq_lens[b] <= max_seq_len (decode),
+ * new tokens + prefix_lens[b] <= max_seq_len (prefill), and the page-table
+ * entries that are read name pages that exist.  Lengths above
+ * max_pages_per_req * 64 are clamped on the device so that the page table is
+ * never read out of bounds.
+ *
+ * Determinism.  For fixed inputs and shapes the results are bitwise
+ * reproducible, and bitwise invariant under a permutation of the physical
+ * pages.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID 1     /* null pointer, non-positive size, inconsistent sizes */
+#define MLA_ERR_UNSUPPORTED 2 /* valid but not implemented: page size, row count, dtype */
+#define MLA_ERR_WORKSPACE 3   /* workspace smaller than mla_splitkv_workspace_size() */
+#define MLA_ERR_HIP 4         /* a HIP runtime call or kernel launch failed */
+
+/* Cache element types. */
+#define MLA_KV_BF16 0
+#define MLA_KV_INT8 1
+
+#define MLA_DIM_QK 576      /* cache row / query row width: 512 latent + 64 rope */
+#define MLA_DIM_V 512       /* value width: the first 512 columns of a row */
+#define MLA_PAGE_SIZE 64    /* the one supported page size */
+#define MLA_MAX_DECODE_ROWS 128 /* q_len * num_heads of one decode request */
+#define MLA_MAX_HEADS 128   /* prefill: heads of one query token */
+
+/*
+ * Workspace bytes for mla_decode and mla_prefill_varlen
+ * [TALK, section "Kernel：让 MLA 真正跑满 GPU": the split parameters and the
+ * workspace size are computed at run time and cached].
+ *
+ * One function serves both entry points.  For decode pass
+ * max_q_len = q_len and total_q = batch * q_len; for prefill pass the
+ * largest and the total number of new tokens.  The result is an upper bound
+ * that depends only on these scalars and the current device's compute-unit
+ * count, never on device-resident lengths, so a buffer sized once serves
+ * every call with the same or smaller arguments.  It may be 0.
+ *
+ * Returns MLA_OK, MLA_ERR_INVALID (bytes_out NULL, a size < 1,
+ * total_q < max_q_len), MLA_ERR_UNSUPPORTED (kv_dtype), or MLA_ERR_HIP when
+ * the device cannot be queried.
+ */
+int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int total_q,
+                               int max_seq_len, int kv_dtype, size_t* bytes_out);
+
+/*
+ * Decode: each of `batch` requests appends q_len query tokens (one new token
+ * plus q_len - 1 speculative drafts, causal among themselves).
+ *
+ * The q_len tokens are folded into the head axis, so one request is a block
+ * of q_len * num_heads query rows (row i * num_heads + h is head h of token
+ * i) against one latent row per cached token [NEWS, section
+ * "TokenSpeed 性能預覽": the decode kernel folds the query-sequence axis into
+ * the head axis; TALK, section "Kernel：让 MLA 真正跑满 GPU": fold factor].
+ * The cached rows are split across compute units and the partial results
+ * (normalised output plus log-sum-exp) are reduced in a second phase [TALK,
+ * same section: two-phase split-KV].
+ *
+ *   q          bf16 [batch * q_len, num_heads, 576]; token b * q_len + i is
+ *              draft i of request b
+ *   kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req: see above
+ *   seq_lens   int32 [batch] on the device: cached rows of request b,
+ *              the q_len new tokens included
+ *   max_seq_len  host upper bound of seq_lens; max_pages_per_req must be
+ *              at least ceil(max_seq_len / 64)
+ *   softmax_scale  multiplies <q, row> (for example 1/sqrt(192))
+ *   out, lse   outputs, [batch * q_len, num_heads, 512] bf16 and
+ *              [batch * q_len, num_heads] fp32
+ *   workspace  device scratch of at least mla_splitkv_workspace_size(batch,
+ *              num_heads, q_len, batch * q_len, max_seq_len, kv_dtype)
+ *              bytes, 256-byte aligned; may be NULL when that size is 0
+ *
+ * Returns MLA_OK; MLA_ERR_INVALID for a null pointer, a size < 1, a
+ * non-finite or non-positive softmax_scale, max_seq_len < q_len or
+ * max_pages_per_req too small; MLA_ERR_UNSUPPORTED for page_size != 64,
+ * q_len * num_heads > 128 or an unknown kv_dtype; MLA_ERR_WORKSPACE;
+ * MLA_ERR_HIP.
+ */
+int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+               const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens,
+               int batch, int q_len, int num_heads, int page_size, int max_seq_len,
+               float softmax_scale, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Variable-length prefill after a cached prefix, without padding
+ * [TALK, section "Kernel：让 MLA 真正跑满 GPU": agent requests hit a cached
+ * prefix and append a few hundred tokens, so Q and KV lengths differ and the
+ * kernel batches variable lengths with no padding].  Work tiles of query
+ * tokens are taken from a device-side queue by a persistent grid so that
+ * uneven requests balance across compute units [TALK, section
+ * "跨平台 Kernel 设计": a persistent prefill kernel balances scheduling on
+ * MI355X].
+ *
+ *   q             bf16 [total_q, num_heads, 576], the new tokens of all
+ *                 requests back to back
+ *   cu_seqlens_q  int32 [batch + 1] on the device: request b owns tokens
+ *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; cu_seqlens_q[0] = 0,
+ *                 cu_seqlens_q[batch] = total_q
+ *   prefix_lens   int32 [batch] on the device: cached rows before the new
+ *                 tokens; request b attends prefix_lens[b] + n_b rows, whose
+ *                 last n_b rows must already hold the new tokens' latent rows
+ *   max_q_len     host upper bound of the new-token counts
+ *   max_seq_len   host upper bound of prefix_lens[b] + n_b
+ *   other arguments as for mla_decode; out/lse are [total_q, num_heads, ...]
+ *   workspace     at least mla_splitkv_workspace_size(batch, num_heads,
+ *                 max_q_len, total_q, max_seq_len, kv_dtype) bytes
+ *
+ * A request with no new tokens writes nothing.  Returns as mla_decode;
+ * num_heads > 128 is MLA_ERR_UNSUPPORTED; total_q = 0 returns MLA_OK
+ * without launching.
+ */
+int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t* prefix_lens,
+                       const void* kv_cache, const float* kv_scale, int kv_dtype,
+                       const int32_t* page_table, int max_pages_per_req, int batch, int total_q,
+                       int max_q_len, int max_seq_len, int num_heads, int page_size,
+                       float softmax_scale, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* hip_stream);
+
+/* Static, human-readable name of a status code. */
+const char* mla_status_string(int status);
+
+/*
+ * The decode split plan the library would use for these scalars on a device
+ * with num_cus compute units (num_cus <= 0: the current device): the number
+ * of phase-one workgroups and the workspace bytes.  Exposed for tests and
+ * tooling; it is the same pure function mla_decode uses.
+ */
+int mla_decode_plan(int batch, int num_heads, int q_len, int max_seq_len, int kv_dtype,
+                    int num_cus, int* phase1_groups, size_t* workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,302 @@
+// C ABI of the MLA library: argument checks, split planning, workspace
+// layout and launches.  See include/mla.h for the contract of each call.
+//
+// Planning follows [TALK "构建面向 Agentic 推理的下一代 LLM 推理引擎", section
+// "Kernel：让 MLA 真正跑满 GPU"]: the split parameters and the workspace size
+// are computed at run time from the shape and cached.  Here the plan is a
+// pure function of (shape scalars, compute-unit count); the cache memoises
+// it per (device, shape) and is guarded by a mutex.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+DecodePlan plan_decode(int batch, int heads, int q_len, int max_seq_len, int kv_dtype, int num_cus) {
+  (void)kv_dtype;
+  DecodePlan p{};
+  const int rows = q_len * heads;
+  p.waves = rows > 64 ? 8 : 4;
+  // One phase-one workgroup per compute unit (each holds two 72 KB pages of
+  // LDS), but at least 4 pages of work per workgroup.
+  const long long pages_max = (long long)batch * ceil_div(max_seq_len, kPage);
+  long long g = num_cus > 0 ? num_cus : 1;
+  const long long cap = (pages_max + 3) / 4;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  p.grid = (int)g;
+  if (p.grid > 1) {
+    const size_t slots = (size_t)(p.grid + batch) * rows;
+    size_t off = 0;
+    p.part_o_off = off;
+    off = align256(off + slots * kDv * sizeof(float));
+    p.part_lse_off = off;
+    off = align256(off + slots * sizeof(float));
+    p.cum_off = off;
+    off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+    p.workspace_bytes = off;
+  }
+  return p;
+}
+
+PrefillPlan plan_prefill(int batch, int heads, int max_q_len, int total_q, int max_seq_len,
+                         int kv_dtype, int num_cus) {
+  (void)max_q_len;
+  (void)total_q;
+  (void)max_seq_len;
+  (void)kv_dtype;
+  PrefillPlan p{};
+  // A work tile is as many whole query tokens as fit in 64 rows (four
+  // waves of 16 rows); a token with more than 64 heads is one tile of up to
+  // 128 rows (eight waves).
+  p.tok_per_tile = heads >= 64 ? 1 : 64 / heads;
+  const int rows = p.tok_per_tile * heads;
+  p.waves = rows > 64 ? 8 : 4;
+  p.grid = num_cus > 0 ? num_cus : 1;
+  size_t off = 0;
+  p.counter_off = off;
+  off = align256(off + sizeof(int32_t));
+  p.order_off = off;
+  off = align256(off + (size_t)batch * sizeof(int32_t));
+  p.tile_cum_off = off;
+  off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+  p.workspace_bytes = off;
+  return p;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+namespace {
+
+std::mutex g_mu;
+std::map<int, int> g_cus;  // device -> compute units
+std::map<std::tuple<int, int, int, int, int, int>, DecodePlan> g_decode_plans;
+
+// Compute units of the current device (MLA_NUM_CUS overrides, for planning
+// without a GPU).  Returns MLA_OK or MLA_ERR_HIP.
+int device_cus(int* dev_out, int* cus_out) {
+  if (const char* env = std::getenv("MLA_NUM_CUS")) {
+    const int v = std::atoi(env);
+    if (v > 0) {
+      *dev_out = -1;
+      *cus_out = v;
+      return MLA_OK;
+    }
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_cus.find(dev);
+    if (it != g_cus.end()) {
+      *dev_out = dev;
+      *cus_out = it->second;
+      return MLA_OK;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_cus[dev] = cus;
+  *dev_out = dev;
+  *cus_out = cus;
+  return MLA_OK;
+}
+
+int cached_decode_plan(int batch, int heads, int q_len, int max_seq_len, int kv_dtype, DecodePlan* out) {
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != MLA_OK) return rc;
+  const auto key = std::make_tuple(dev * 100000 + cus, batch, heads, q_len, max_seq_len, kv_dtype);
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_decode_plans.find(key);
+  if (it == g_decode_plans.end()) {
+    if (g_decode_plans.size() > 4096) g_decode_plans.clear();
+    it = g_decode_plans.emplace(key, plan_decode(batch, heads, q_len, max_seq_len, kv_dtype, cus)).first;
+  }
+  *out = it->second;
+  return MLA_OK;
+}
+
+bool decode_shape(int batch, int num_heads, int max_q_len, int total_q) {
+  return (long long)max_q_len * num_heads <= MLA_MAX_DECODE_ROWS &&
+         (long long)batch * max_q_len == total_q;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int mla_decode_plan(int batch, int num_heads, int q_len, int max_seq_len, int kv_dtype, int num_cus,
+                    int* phase1_groups, size_t* workspace_bytes) {
+  if (!phase1_groups || !workspace_bytes) return MLA_ERR_INVALID;
+  if (batch < 1 || num_heads < 1 || q_len < 1 || max_seq_len < q_len) return MLA_ERR_INVALID;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if ((long long)q_len * num_heads > MLA_MAX_DECODE_ROWS) return MLA_ERR_UNSUPPORTED;
+  DecodePlan p{};
+  if (num_cus > 0) {
+    p = plan_decode(batch, num_heads, q_len, max_seq_len, kv_dtype, num_cus);
+  } else {
+    const int rc = cached_decode_plan(batch, num_heads, q_len, max_seq_len, kv_dtype, &p);
+    if (rc != MLA_OK) return rc;
+  }
+  *phase1_groups = p.grid;
+  *workspace_bytes = p.workspace_bytes;
+  return MLA_OK;
+}
+
+int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int total_q, int max_seq_len,
+                               int kv_dtype, size_t* bytes_out) {
+  if (!bytes_out) return MLA_ERR_INVALID;
+  *bytes_out = 0;
+  if (batch < 1 || num_heads < 1 || max_q_len < 0 || total_q < max_q_len || max_seq_len < 1)
+    return MLA_ERR_INVALID;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != MLA_OK) return rc;
+  size_t bytes = 0;
+  if (max_q_len >= 1 && max_seq_len >= max_q_len && decode_shape(batch, num_heads, max_q_len, total_q)) {
+    DecodePlan d{};
+    const int rc2 = cached_decode_plan(batch, num_heads, max_q_len, max_seq_len, kv_dtype, &d);
+    if (rc2 != MLA_OK) return rc2;
+    bytes = d.workspace_bytes;
+  }
+  if (num_heads <= MLA_MAX_HEADS) {
+    const PrefillPlan pp = plan_prefill(batch, num_heads, max_q_len, total_q, max_seq_len, kv_dtype, cus);
+    if (pp.workspace_bytes > bytes) bytes = pp.workspace_bytes;
+  }
+  *bytes_out = bytes;
+  return MLA_OK;
+}
+
+int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+               const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens, int batch,
+               int q_len, int num_heads, int page_size, int max_seq_len, float softmax_scale, void* out,
+               float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  // ---- host-scalar checks, before any HIP call ----
+  if (!q || !kv_cache || !page_table || !seq_lens || !out || !lse) return MLA_ERR_INVALID;
+  if (batch < 1 || q_len < 1 || num_heads < 1 || max_pages_per_req < 1 || max_seq_len < 1)
+    return MLA_ERR_INVALID;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype == MLA_KV_INT8 && !kv_scale) return MLA_ERR_INVALID;
+  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if ((long long)q_len * num_heads > MLA_MAX_DECODE_ROWS) return MLA_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID;
+  if (max_seq_len < q_len) return MLA_ERR_INVALID;
+  if ((long long)max_pages_per_req * MLA_PAGE_SIZE < max_seq_len) return MLA_ERR_INVALID;
+  if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if ((long long)batch * q_len * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_INVALID;
+  if (kv_dtype == MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;  // int8 kernels: not built yet
+
+  DecodePlan plan{};
+  const int rc = cached_decode_plan(batch, num_heads, q_len, max_seq_len, kv_dtype, &plan);
+  if (rc != MLA_OK) return rc;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return MLA_ERR_WORKSPACE;
+
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.max_pages = max_pages_per_req;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.heads = num_heads;
+  a.rows = q_len * num_heads;
+  a.grid = plan.grid;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  if (plan.grid > 1) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws + plan.part_o_off);
+    a.part_lse = reinterpret_cast<float*>(ws + plan.part_lse_off);
+    a.cum_pages = reinterpret_cast<int32_t*>(ws + plan.cum_off);
+  }
+  const hipError_t e = launch_decode(plan, a, kv_dtype, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t* prefix_lens,
+                       const void* kv_cache, const float* kv_scale, int kv_dtype,
+                       const int32_t* page_table, int max_pages_per_req, int batch, int total_q,
+                       int max_q_len, int max_seq_len, int num_heads, int page_size, float softmax_scale,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!q || !cu_seqlens_q || !prefix_lens || !kv_cache || !page_table || !out || !lse)
+    return MLA_ERR_INVALID;
+  if (batch < 1 || num_heads < 1 || max_pages_per_req < 1 || total_q < 0 || max_q_len < 0 ||
+      max_seq_len < 1)
+    return MLA_ERR_INVALID;
+  if (total_q < max_q_len || max_seq_len < max_q_len) return MLA_ERR_INVALID;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype == MLA_KV_INT8 && !kv_scale) return MLA_ERR_INVALID;
+  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (num_heads > MLA_MAX_HEADS) return MLA_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID;
+  if ((long long)max_pages_per_req * MLA_PAGE_SIZE < max_seq_len) return MLA_ERR_INVALID;
+  if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if ((long long)total_q * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_INVALID;
+  if (kv_dtype == MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;  // int8 kernels: not built yet
+  if (total_q == 0) return MLA_OK;
+
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != MLA_OK) return rc;
+  const PrefillPlan plan = plan_prefill(batch, num_heads, max_q_len, total_q, max_seq_len, kv_dtype, cus);
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return MLA_ERR_WORKSPACE;
+
+  PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.cu_seqlens = cu_seqlens_q;
+  a.prefix_lens = prefix_lens;
+  a.kv = static_cast<const uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_req;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.heads = num_heads;
+  a.tok_per_tile = plan.tok_per_tile;
+  a.grid = plan.grid;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.counter = reinterpret_cast<int32_t*>(ws + plan.counter_off);
+  a.order = reinterpret_cast<int32_t*>(ws + plan.order_off);
+  a.tile_cum = reinterpret_cast<int32_t*>(ws + plan.tile_cum_off);
+  const hipError_t e = launch_prefill(plan, a, kv_dtype, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+// MLA decode over a paged latent cache: split-KV phase one and the merge.
+//
+// Sources (web pages on the TokenSpeed inference engine):
+//   [TALK] "构建面向 Agentic 推理的下一代 LLM 推理引擎", AICon 2026 talk
+//          transcript, section "Kernel：让 MLA 真正跑满 GPU": query x latent
+//          key is the first product; decode is bandwidth-bound even at long
+//          prefixes; query tokens are folded into the head axis; split-KV runs
+//          as a partial phase and a reduction phase with a runtime-computed
+//          split and workspace.
+//   [NEWS] "英偉達力薦，小團隊兩個月開源一款「光速級」智能體推理引擎", section
+//          "TokenSpeed 性能預覽": the decode kernel folds the query-sequence
+//          axis into the head axis to fill the M tile of the first product.
+//
+// Decomposition.  Request b's q_len * heads query rows form one block
+// (contiguous in memory, so the fold is free).  All requests' cache pages
+// are laid end to end in one stream of P pages and phase one gives each of
+// its G workgroups an equal, contiguous share floor(g*P/G) .. floor((g+1)*P/G)
+// of that stream, whatever the per-request lengths are: a short request
+// costs no idle workgroups and a long one is spread over many.  A
+// workgroup that meets several requests in its share produces one partial
+// (normalised output and log2-sum-exp of its rows) per request; workgroup g
+// stores its partial for request b in slot g + b, which is unique because a
+// share that reaches request b + 1 cannot reach back into request b - 1.
+// The merge then reduces, per request, the partials of the workgroups whose
+// shares intersect it.  Every cache byte is read from HBM once per call,
+// and each page is read by one workgroup for all the request's rows.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+constexpr int kWin = 128;  // pages per window of the per-workgroup page list
+
+__device__ __forceinline__ int clamp_len(int L, int max_pages) {
+  L = L < 0 ? 0 : L;
+  const int cap = max_pages * kPage;
+  return L > cap ? cap : L;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
+// First workgroup whose share contains global page p (shares are
+// floor(g*P/G) .. floor((g+1)*P/G); the largest g with start <= p).
+__device__ __forceinline__ int owner_group(long long p, long long P, int G) {
+  return (int)(((p + 1) * G - 1) / P);
+}
+
+// Write the rows of one finished (request, share) pair: the final output
+// when phase one is the only phase, else the partial in slot `slot`.
+__device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& st, int b, int slot,
+                                           int row, bool row_ok, int lane) {
+  float inv, lse2;
+  finish_row(st, inv, lse2);
+  if (!row_ok) return;
+  const int g = lane >> 4;
+  if (a.grid == 1) {
+    uint16_t* dst = a.out + ((size_t)b * a.rows + row) * kDv + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < kOFrags; ++ct) {
+      const f32x4 v = st.o[ct] * inv;
+      bf16x4 h;
+      h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+      *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
+    }
+    if (g == 0) a.lse[(size_t)b * a.rows + row] = lse2 * kLn2;
+  } else {
+    float* dst = a.part_o + ((size_t)slot * a.rows + row) * kDv + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < kOFrags; ++ct) *reinterpret_cast<f32x4*>(dst + 16 * ct) = st.o[ct] * inv;
+    if (g == 0) a.part_lse[(size_t)slot * a.rows + row] = lse2;
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void decode_phase1(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[2 * kTileBytes];
+  MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)tiles_raw;
+  __shared__ int s_pid[kWin], s_req[kWin], s_rem[kWin];
+  __shared__ int s_info[4];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int G = a.grid;
+  const int g = blockIdx.x;
+
+  // ---- locate this workgroup's share of the page stream (wave 0) ----
+  if (w == 0) {
+    long long P = 0;
+    for (int base = 0; base < a.batch; base += 64) {
+      const int b = base + lane;
+      const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
+      const int incl = wave_incl_scan(np, lane);
+      if (g == 0 && G > 1 && b < a.batch) a.cum_pages[b] = (int)(P + incl - np);
+      P += __shfl(incl, 63);
+    }
+    if (g == 0 && G > 1 && lane == 0) a.cum_pages[a.batch] = (int)P;
+    const long long lo = P * g / G, hi = P * (g + 1) / G;
+    int b0 = a.batch, j0 = 0;
+    if (lo < hi) {
+      long long run = 0;
+      for (int base = 0; base < a.batch; base += 64) {
+        const int b = base + lane;
+        const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
+        const int incl = wave_incl_scan(np, lane);
+        const long long before = run + incl - np;
+        const bool hit = np > 0 && before <= lo && lo < before + np;
+        const unsigned long long mask = __ballot(hit);
+        if (mask) {
+          const int src = __ffsll((long long)mask) - 1;
+          b0 = base + src;
+          j0 = (int)(lo - (run + __shfl(incl - np, src)));
+          break;
+        }
+        run += __shfl(incl, 63);
+      }
+    }
+    if (lane == 0) {
+      s_info[0] = (int)lo;
+      s_info[1] = (int)hi;
+      s_info[2] = b0;
+      s_info[3] = j0;
+    }
+  }
+  __syncthreads();
+  const int seg_lo = s_info[0], seg_hi = s_info[1];
+  if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
+  int cb = s_info[2], cj = s_info[3];
+
+  // ---- this wave's 16 query rows ----
+  const int row = 16 * w + (lane & 15);
+  const bool wave_rows = 16 * w < a.rows;
+  const bool row_ok = row < a.rows;
+  const int draft = row_ok ? row / a.heads : 0;  // token index i of this row within its request
+  const int late = a.q_len - draft;              // row sees rows t <= L - late
+
+  RowState st;
+  bf16x8 qf[kQFrags];
+  int cur_b = -1;
+
+  for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
+    const int n = min(kWin, seg_hi - wlo);
+    __syncthreads();  // the previous window's list and stages are no longer read
+    for (int k = threadIdx.x; k < n; k += NW * 64) {
+      int b = cb, off = cj + k, Lc;
+      for (;;) {
+        Lc = clamp_len(a.seq_lens[b], a.max_pages);
+        const int np = (Lc + kPage - 1) / kPage;
+        if (off < np || b + 1 >= a.batch) break;
+        off -= np;
+        ++b;
+      }
+      off = min(off, a.max_pages - 1);  // never past the table, whatever the lengths say
+      s_pid[k] = a.page_table[(size_t)b * a.max_pages + off];
+      s_req[k] = b;
+      s_rem[k] = Lc - kPage * off;
+    }
+    {  // advance the window cursor by n pages (uniform across the workgroup)
+      int b = cb, off = cj + n;
+      for (;;) {
+        const int np = (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage;
+        if (off < np || b + 1 >= a.batch) break;
+        off -= np;
+        ++b;
+      }
+      cb = b;
+      cj = off;
+    }
+    __syncthreads();
+
+    stage_page<NW>(a.kv + (size_t)s_pid[0] * kPageBytes, tiles, min(kPage, s_rem[0]), w, lane);
+    for (int k = 0; k < n; ++k) {
+      const int b = s_req[k];
+      if (b != cur_b) {
+        if (cur_b >= 0 && wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, lane);
+        cur_b = b;
+        if (wave_rows) {
+          load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+          reset_state(st);
+        }
+      }
+      const int rem = s_rem[k];
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of page k have landed in LDS
+      __syncthreads();                // ... and every other wave's; page k-1's stage is free
+      if (k + 1 < n)
+        stage_page<NW>(a.kv + (size_t)s_pid[k + 1] * kPageBytes, tiles + ((k + 1) & 1) * kTileBytes,
+                   min(kPage, s_rem[k + 1]), w, lane);
+      if (wave_rows) attend_page(tiles + (k & 1) * kTileBytes, qf, rem - late, a.scale_log2, lane, st);
+    }
+  }
+  if (wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, lane);
+}
+
+// Phase two: per (request, row), reduce the partials of the workgroups
+// whose shares intersect the request.  One wave per row; lane owns 8
+// consecutive value columns.
+__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int R = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (R >= a.batch * a.rows) return;
+  const int b = R / a.rows, row = R - b * a.rows;
+  const long long P = a.cum_pages[a.batch];
+  const int G = a.grid;
+  const long long p0 = a.cum_pages[b], p1 = a.cum_pages[b + 1];
+  if (p1 <= p0) return;
+  const int g0 = owner_group(p0, P, G), g1 = owner_group(p1 - 1, P, G);
+
+  float m = -INFINITY;
+  for (int gg = g0; gg <= g1; ++gg) {
+    if (P * gg / G >= P * (gg + 1) / G) continue;  // empty share: wrote nothing
+    m = fmaxf(m, a.part_lse[(size_t)(gg + b) * a.rows + row]);
+  }
+  const float m_use = m == -INFINITY ? 0.f : m;
+  float wsum = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int gg = g0; gg <= g1; ++gg) {
+    if (P * gg / G >= P * (gg + 1) / G) continue;
+    const size_t slot = (size_t)(gg + b) * a.rows + row;
+    const float wgt = fast_exp2(a.part_lse[slot] - m_use);
+    wsum += wgt;
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + slot * kDv + 8 * lane);
+    acc0 += src[0] * wgt;
+    acc1 += src[1] * wgt;
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  acc0 *= inv;
+  acc1 *= inv;
+  bf16x8 h;
+  h[0] = (__bf16)acc0[0]; h[1] = (__bf16)acc0[1]; h[2] = (__bf16)acc0[2]; h[3] = (__bf16)acc0[3];
+  h[4] = (__bf16)acc1[0]; h[5] = (__bf16)acc1[1]; h[6] = (__bf16)acc1[2]; h[7] = (__bf16)acc1[3];
+  *reinterpret_cast<bf16x8*>(a.out + (size_t)R * kDv + 8 * lane) = h;
+  if (lane == 0) a.lse[R] = wsum > 0.f ? (m_use + fast_log2(wsum)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream) {
+  (void)kv_dtype;
+  if (plan.waves == 8)
+    hipLaunchKernelGGL(decode_phase1<8>, dim3(plan.grid), dim3(512), 0, stream, args);
+  else
+    hipLaunchKernelGGL(decode_phase1<4>, dim3(plan.grid), dim3(256), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.grid == 1) return e;
+  const int total_rows = args.batch * args.rows;
+  hipLaunchKernelGGL(decode_merge, dim3((total_rows + 3) / 4), dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,81 @@
+// Host-side structures shared between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDqk = 576;                      // row width: 512 latent + 64 rope
+constexpr int kDv = 512;                       // value width
+constexpr int kPage = 64;                      // rows per page (= one LDS tile)
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Arguments of the decode kernels (passed by value as kernel arguments).
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [batch * q_len, heads, 576]
+  const uint8_t* kv;          // pages, bf16 or int8 rows
+  const float* kv_scale;      // int8 only
+  const int32_t* page_table;  // [batch, max_pages]
+  const int32_t* seq_lens;    // [batch]
+  int max_pages;
+  int batch;
+  int q_len;
+  int heads;
+  int rows;                   // q_len * heads: folded query rows of one request
+  int grid;                   // phase-one workgroups
+  float scale_log2;           // softmax_scale * log2(e)
+  uint16_t* out;              // bf16 [batch * rows, 512]
+  float* lse;                 // fp32 [batch * rows]
+  float* part_o;              // workspace: [(grid + batch) * rows, 512]
+  float* part_lse;            // workspace: [(grid + batch) * rows], log2 units
+  int32_t* cum_pages;         // workspace: [batch + 1] page prefix sums
+};
+
+// Arguments of the prefill kernels.
+struct PrefillArgs {
+  const uint16_t* q;          // bf16 [total_q, heads, 576]
+  const int32_t* cu_seqlens;  // [batch + 1]
+  const int32_t* prefix_lens; // [batch]
+  const uint8_t* kv;
+  const float* kv_scale;
+  const int32_t* page_table;
+  int max_pages;
+  int batch;
+  int total_q;
+  int heads;
+  int tok_per_tile;           // query tokens per work tile (tile rows = tok_per_tile * heads)
+  int grid;
+  float scale_log2;
+  uint16_t* out;
+  float* lse;
+  int32_t* order;             // workspace: [batch] requests, most expensive first
+  int32_t* tile_cum;          // workspace: [batch + 1] cumulative tiles in that order
+  int32_t* counter;           // workspace: work-queue head
+};
+
+struct DecodePlan {
+  int grid;                   // phase-one workgroups (1: single pass, no merge)
+  int waves;                  // waves per workgroup (4 or 8)
+  size_t part_o_off, part_lse_off, cum_off;
+  size_t workspace_bytes;
+};
+
+struct PrefillPlan {
+  int grid;
+  int waves;
+  int tok_per_tile;
+  size_t order_off, tile_cum_off, counter_off;
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(int batch, int heads, int q_len, int max_seq_len, int kv_dtype, int num_cus);
+PrefillPlan plan_prefill(int batch, int heads, int max_q_len, int total_q, int max_seq_len,
+                         int kv_dtype, int num_cus);
+
+hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream);
+hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,183 @@
+// Variable-length MLA prefill over a paged latent cache, persistent grid.
+//
+// Sources (web pages on the TokenSpeed inference engine):
+//   [TALK] "构建面向 Agentic 推理的下一代 LLM 推理引擎", AICon 2026 talk
+//          transcript.  Section "Kernel：让 MLA 真正跑满 GPU": agent requests
+//          hit a cached prefix and append a few hundred tokens, so Q and KV
+//          lengths differ per request and the kernel batches them with no
+//          padding.  Section "跨平台 Kernel 设计": on MI355X a persistent
+//          prefill kernel balances the scheduling across compute units.
+//
+// Work decomposition.  A work tile is up to `tok_per_tile` consecutive new
+// tokens of one request (tok_per_tile * heads <= 128 query rows, one wave per
+// 16 rows).  Its cost is proportional to the cached rows its last token sees
+// (prefix + position + 1).  A one-workgroup kernel orders the requests by the
+// cost of their most expensive tile, most expensive first, and lays out the
+// cumulative tile counts in that order; the tiles of a request are handed out
+// last-token-first.  A persistent grid of one workgroup per compute unit then
+// takes tiles from an atomic counter until the list is exhausted: the long
+// tiles start first and the short ones fill the tail (longest processing
+// time first).  Every tile streams its request's pages 0 .. through the same
+// LDS pipeline as decode; only the pages that hold a row some query token of
+// the tile can see are read, and only the diagonal pages are masked.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+constexpr int kPWin = 128;  // page ids staged per window
+
+__device__ __forceinline__ int p_clamp(int L, int max_pages) {
+  L = L < 0 ? 0 : L;
+  const int cap = max_pages * kPage;
+  return L > cap ? cap : L;
+}
+
+// One workgroup: order requests by tile cost, lay out cumulative tile
+// counts, reset the queue head.
+__global__ __launch_bounds__(256) void prefill_worklist(PrefillArgs a) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // rank sort by cost (descending), ties by request index
+  for (int b = tid; b < a.batch; b += 256) {
+    const int n = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+    const long long cb = n > 0 ? (long long)a.prefix_lens[b] + n : -1;
+    int rank = 0;
+    for (int o = 0; o < a.batch; ++o) {
+      const int no = a.cu_seqlens[o + 1] - a.cu_seqlens[o];
+      const long long co = no > 0 ? (long long)a.prefix_lens[o] + no : -1;
+      rank += (co > cb) || (co == cb && o < b);
+    }
+    a.order[rank] = b;
+  }
+  if (tid == 0) *a.counter = 0;
+  __syncthreads();
+  if (tid < 64) {
+    int run = 0;
+    for (int base = 0; base < a.batch; base += 64) {
+      const int k = base + lane;
+      int nt = 0;
+      if (k < a.batch) {
+        const int b = a.order[k];
+        const int n = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+        nt = n > 0 ? (n + a.tok_per_tile - 1) / a.tok_per_tile : 0;
+      }
+      int incl = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      if (k < a.batch) a.tile_cum[k] = run + incl - nt;
+      run += __shfl(incl, 63);
+    }
+    if (lane == 0) a.tile_cum[a.batch] = run;
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_persistent(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[2 * kTileBytes];
+  MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)tiles_raw;
+  __shared__ int s_pid[kPWin];
+  __shared__ int s_tile;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int total_tiles = a.tile_cum[a.batch];
+  const int rows_per_tile = a.tok_per_tile * a.heads;
+  const int row = 16 * w + (lane & 15);
+  const bool wave_rows = 16 * w < rows_per_tile;
+  const int tok_in_tile = row / a.heads;  // may exceed the tile's token count (then masked off)
+  const int head = row - tok_in_tile * a.heads;
+
+  RowState st;
+  bf16x8 qf[kQFrags];
+
+  for (;;) {
+    __syncthreads();  // previous tile fully done (stages, page list, s_tile)
+    if (threadIdx.x == 0) s_tile = atomicAdd(a.counter, 1);
+    __syncthreads();
+    const int t = s_tile;
+    if (t >= total_tiles) break;
+
+    // locate the tile: order position k with tile_cum[k] <= t < tile_cum[k+1]
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tile_cum[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int b = a.order[lo];
+    const int q0 = a.cu_seqlens[b];
+    const int n_b = a.cu_seqlens[b + 1] - q0;
+    const int ntiles = (n_b + a.tok_per_tile - 1) / a.tok_per_tile;
+    const int jt = ntiles - 1 - (t - a.tile_cum[lo]);  // last tiles first
+    const int j0 = jt * a.tok_per_tile;                 // first new token of the tile
+    const int j1 = min(n_b, j0 + a.tok_per_tile);       // one past its last
+    const int P_b = a.prefix_lens[b];
+    const int L_b = p_clamp(P_b + n_b, a.max_pages);
+    const int kv_end = min(L_b, P_b + j1);              // rows the tile's last token sees
+    const int npages = (kv_end + kPage - 1) / kPage;
+
+    const int j = j0 + tok_in_tile;                     // this lane's new-token index
+    const bool row_ok = wave_rows && tok_in_tile < a.tok_per_tile && j < j1;
+    const int tok = q0 + j;
+    const int vis_last = P_b + j;                       // last visible row of this query token
+    if (wave_rows) {
+      load_q(row_ok ? a.q + ((size_t)tok * a.heads + head) * kDqk : nullptr, lane, qf);
+      reset_state(st);
+    }
+
+    for (int plo = 0; plo < npages; plo += kPWin) {
+      const int n = min(kPWin, npages - plo);
+      __syncthreads();
+      for (int k = threadIdx.x; k < n; k += NW * 64)
+        s_pid[k] = a.page_table[(size_t)b * a.max_pages + plo + k];
+      __syncthreads();
+      stage_page<NW>(a.kv + (size_t)s_pid[0] * kPageBytes, tiles, min(kPage, kv_end - kPage * plo), w, lane);
+      for (int k = 0; k < n; ++k) {
+        const int pg = plo + k;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (k + 1 < n)
+          stage_page<NW>(a.kv + (size_t)s_pid[k + 1] * kPageBytes, tiles + ((k + 1) & 1) * kTileBytes,
+                     min(kPage, kv_end - kPage * (pg + 1)), w, lane);
+        if (wave_rows) {
+          const int lim = row_ok ? vis_last - kPage * pg : -1;
+          attend_page(tiles + (k & 1) * kTileBytes, qf, lim, a.scale_log2, lane, st);
+        }
+      }
+    }
+
+    if (wave_rows) {
+      float inv, lse2;
+      finish_row(st, inv, lse2);
+      if (row_ok) {
+        const int g = lane >> 4;
+        uint16_t* dst = a.out + ((size_t)tok * a.heads + head) * kDv + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < kOFrags; ++ct) {
+          const f32x4 v = st.o[ct] * inv;
+          bf16x4 h;
+          h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+          *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
+        }
+        if (g == 0) a.lse[(size_t)tok * a.heads + head] = lse2 * kLn2;
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream) {
+  (void)kv_dtype;
+  hipLaunchKernelGGL(prefill_worklist, dim3(1), dim3(256), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (plan.waves == 8)
+    hipLaunchKernelGGL(prefill_persistent<8>, dim3(plan.grid), dim3(512), 0, stream, args);
+  else
+    hipLaunchKernelGGL(prefill_persistent<4>, dim3(plan.grid), dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace mla

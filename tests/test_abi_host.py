@@ -1,0 +1,125 @@
+"""The C-ABI library on the host: it loads, exports what include/mla.h declares,
+and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_attention_paged_amd as mla
+from mla_attention_paged_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        _build.build()
+    os.environ["MLA_NUM_CUS"] = "256"
+    return mla.library()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"mla_decode", "mla_prefill_varlen", "mla_splitkv_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert mla.mla_status_string(code) not in ("", "unknown status")
+    assert mla.mla_status_string(99) == "unknown status"
+
+
+def _decode_rc(lib, **kw):
+    a = dict(q=1, kv=1, scale=None, kind=0, pt=1, maxp=1024, lens=1, batch=4, q_len=4, heads=16, page=64,
+             maxlen=65536, scale_f=0.07, out=1, lse=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.mla_decode(a["q"], a["kv"], a["scale"], a["kind"], a["pt"], a["maxp"], a["lens"], a["batch"],
+                          a["q_len"], a["heads"], a["page"], a["maxlen"], a["scale_f"], a["out"], a["lse"],
+                          a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), mla.MLA_ERR_INVALID),
+    (dict(kv=None), mla.MLA_ERR_INVALID),
+    (dict(pt=None), mla.MLA_ERR_INVALID),
+    (dict(lens=None), mla.MLA_ERR_INVALID),
+    (dict(out=None), mla.MLA_ERR_INVALID),
+    (dict(lse=None), mla.MLA_ERR_INVALID),
+    (dict(batch=0), mla.MLA_ERR_INVALID),
+    (dict(q_len=0), mla.MLA_ERR_INVALID),
+    (dict(heads=0), mla.MLA_ERR_INVALID),
+    (dict(page=32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(kind=2), mla.MLA_ERR_UNSUPPORTED),
+    (dict(kind=1), mla.MLA_ERR_INVALID),            # int8 without scales
+    (dict(q_len=9, heads=16), mla.MLA_ERR_UNSUPPORTED),  # 144 folded rows
+    (dict(scale_f=0.0), mla.MLA_ERR_INVALID),
+    (dict(scale_f=float("nan")), mla.MLA_ERR_INVALID),
+    (dict(maxlen=3), mla.MLA_ERR_INVALID),          # shorter than q_len
+    (dict(maxp=1023), mla.MLA_ERR_INVALID),         # table narrower than max_seq_len
+    (dict(ws=8), mla.MLA_ERR_INVALID),              # misaligned workspace
+    (dict(ws=None, wsb=0), mla.MLA_ERR_WORKSPACE),  # plan needs a workspace
+])
+def test_decode_argument_checks(lib, kw, code):
+    assert _decode_rc(lib, **kw) == code
+
+
+def test_prefill_argument_checks(lib):
+    def rc(**kw):
+        a = dict(q=1, cu=1, prefix=1, kv=1, scale=None, kind=0, pt=1, maxp=64, batch=2, tq=10, mq=6, maxlen=4096,
+                 heads=16, page=64, sf=0.07, out=1, lse=1, ws=None, wsb=0)
+        a.update(kw)
+        return lib.mla_prefill_varlen(a["q"], a["cu"], a["prefix"], a["kv"], a["scale"], a["kind"], a["pt"],
+                                      a["maxp"], a["batch"], a["tq"], a["mq"], a["maxlen"], a["heads"], a["page"],
+                                      a["sf"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+    assert rc(cu=None) == mla.MLA_ERR_INVALID
+    assert rc(prefix=None) == mla.MLA_ERR_INVALID
+    assert rc(heads=129) == mla.MLA_ERR_UNSUPPORTED
+    assert rc(page=16) == mla.MLA_ERR_UNSUPPORTED
+    assert rc(tq=5, mq=6) == mla.MLA_ERR_INVALID
+    assert rc(maxp=63) == mla.MLA_ERR_INVALID
+    assert rc(ws=None) == mla.MLA_ERR_WORKSPACE
+    assert rc(tq=0, mq=0) == mla.MLA_OK                # nothing to do, no launch
+
+
+def test_decode_plan_shapes(lib):
+    # 64K-row decode, 4 requests: one phase-one workgroup per compute unit
+    g, ws = mla.mla_decode_plan(4, 16, 4, 65536, 0, num_cus=256)
+    assert g == 256 and ws >= (256 + 4) * 64 * 513 * 4
+    # 256 rows: a single workgroup writes the output directly, no workspace
+    assert mla.mla_decode_plan(1, 16, 1, 256, 0, num_cus=256) == (1, 0)
+    # at least four pages per workgroup
+    g, _ = mla.mla_decode_plan(2, 16, 1, 640, 0, num_cus=256)
+    assert g == 5
+    # more rows per request (q_len * heads > 64) still plans
+    g, ws = mla.mla_decode_plan(2, 32, 4, 8192, 0, num_cus=256)
+    assert g == 64 and ws > 0
+
+
+def test_workspace_size_is_monotone_and_covers_plan(lib):
+    prev = 0
+    for L in (64, 256, 1024, 8192, 65536, 262144):
+        ws = mla.mla_splitkv_workspace_size(4, 16, 4, 16, L, 0)
+        assert ws >= prev
+        assert ws >= mla.mla_decode_plan(4, 16, 4, L, 0, num_cus=256)[1]
+        prev = ws
+    # prefill shapes need only the small work-list area
+    assert 0 < mla.mla_splitkv_workspace_size(8, 16, 2000, 8629, 100304, 0) < 1 << 20
+
+
+def test_workspace_size_argument_checks(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 0, None) == mla.MLA_ERR_INVALID
+    assert lib.mla_splitkv_workspace_size(0, 16, 4, 16, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
+    assert lib.mla_splitkv_workspace_size(4, 16, 4, 3, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
+    assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 7, ctypes.byref(out)) == mla.MLA_ERR_UNSUPPORTED

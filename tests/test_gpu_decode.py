@@ -1,0 +1,216 @@
+"""Decode parity: the HIP path through the C ABI against the fp64 oracle (GPU)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mla_attention_paged_amd as mla
+import oracle
+import synth
+from mla_gpu import assert_close, decode_inputs, host, run_decode
+
+pytestmark = pytest.mark.gpu
+
+BF16_ONE = 0x3F80
+
+
+def _put_row(case, b, t, values_bits):
+    c = case.cache
+    page = c.page_table[b, t // 64]
+    c.data[page, t % 64] = values_bits
+
+
+def _row_bits(case, b, t):
+    c = case.cache
+    return c.data[c.page_table[b, t // 64], t % 64]
+
+
+class _cus:
+    """Temporarily plan for a different compute-unit count (changes the split)."""
+
+    def __init__(self, n):
+        self.n = n
+
+    def __enter__(self):
+        self.old = os.environ.get("MLA_NUM_CUS")
+        os.environ["MLA_NUM_CUS"] = str(self.n)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("MLA_NUM_CUS", None)
+        else:
+            os.environ["MLA_NUM_CUS"] = self.old
+
+
+SMALL = [
+    # (seed, batch, heads, q_len, seq_lens)
+    (101, 1, 16, 1, [256]),
+    (102, 2, 16, 4, [300, 129]),
+    (103, 3, 16, 2, [64, 65, 1000]),
+    (104, 4, 32, 2, [17, 200, 640, 2051]),
+    (105, 1, 8, 1, [1]),
+    (106, 2, 4, 3, [3, 70]),
+    (107, 5, 16, 4, [4, 5, 63, 64, 127]),
+    (108, 2, 64, 1, [700, 90]),
+    (109, 1, 1, 1, [333]),
+]
+
+
+@pytest.mark.parametrize("seed,batch,heads,q_len,lens", SMALL, ids=[str(s[0]) for s in SMALL])
+def test_decode_matches_oracle_small(seed, batch, heads, q_len, lens):
+    case = synth.make_decode_case(seed, batch, heads, q_len, seq_lens=lens)
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, f"seed {seed}")
+
+
+@pytest.mark.parametrize("cus", [1, 2, 3, 7, 64, 256, 1024])
+def test_decode_split_plans_agree(cus):
+    """Different compute-unit counts give different splits; all match the oracle."""
+    case = synth.make_decode_case(201, 3, 16, 4, seq_lens=[1500, 64, 777])
+    with _cus(cus):
+        out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, f"cus {cus}")
+
+
+def test_decode_workload0_full():
+    case = synth.make_workload(0)
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, case.name)
+
+
+def test_decode_ragged_many_requests():
+    g = np.random.default_rng(5)
+    lens = g.integers(2, 3000, size=37)
+    case = synth.make_decode_case(202, 37, 16, 2, seq_lens=lens, max_seq_len=4096)
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, "ragged 37")
+
+
+@pytest.mark.parametrize("cus", [1, 5, 256])
+def test_decode_needle_bit_exact(cus):
+    """q = 64 e_j and one row with value 32 at dim j: the needle's score leads every
+    other by > 100 (natural units), all other weights underflow to 0 in fp32 and the
+    output must be the needle's value columns bit for bit."""
+    L = 3 * 64 + 17
+    positions = [0, 63, 64, 127, 128, L - 1]
+    batch = len(positions)
+    case = synth.make_decode_case(301, batch, 16, 1, seq_lens=[L] * batch)
+    g = np.random.default_rng(7)
+    js = g.integers(0, 512, size=(batch, 16))
+    for b, pos in enumerate(positions):
+        for h in range(16):
+            q = np.zeros(576, np.uint16)
+            q[js[b, h]] = synth.bf16_bits(np.array([64.0], np.float32))[0]
+            case.q[b, h] = q
+        row = _row_bits(case, b, pos).copy()
+        for h in range(16):
+            row[js[b, h]] = synth.bf16_bits(np.array([32.0], np.float32))[0]
+        _put_row(case, b, pos, row)
+    with _cus(cus):
+        out, lse = run_decode(case)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, pos in enumerate(positions):
+        want = _row_bits(case, b, pos)[:512]
+        for h in range(16):
+            assert np.array_equal(got[b, h], want), f"needle at {pos}, head {h}"
+
+
+def test_decode_causal_needle():
+    """A needle at row L-q+k is seen bit-exactly by drafts i >= k; drafts i < k match the oracle."""
+    q_len, L, k = 4, 300, 2
+    case = synth.make_decode_case(302, 1, 16, q_len, seq_lens=[L])
+    pos = L - q_len + k
+    j = 5
+    for i in range(q_len):
+        for h in range(16):
+            qq = np.zeros(576, np.uint16)
+            qq[j] = synth.bf16_bits(np.array([64.0], np.float32))[0]
+            case.q[i, h] = qq
+    row = _row_bits(case, 0, pos).copy()
+    row[j] = synth.bf16_bits(np.array([32.0], np.float32))[0]
+    _put_row(case, 0, pos, row)
+    out, lse = run_decode(case)
+    torch.cuda.synchronize()
+    bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for i in range(k, q_len):
+        for h in range(16):
+            assert np.array_equal(bits[i, h], _row_bits(case, 0, pos)[:512])
+    ref_out, ref_lse = oracle.decode(case, tokens=list(range(k)))
+    o, l_ = host(out, lse)
+    assert_close(o[:k], l_[:k], ref_out, ref_lse, "drafts before the needle")
+
+
+def test_decode_single_row_is_that_row():
+    case = synth.make_decode_case(303, 3, 16, 1, seq_lens=[1, 1, 1])
+    out, lse = run_decode(case)
+    torch.cuda.synchronize()
+    bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(3):
+        for h in range(16):
+            assert np.array_equal(bits[b, h], _row_bits(case, b, 0)[:512])
+    ref_out, ref_lse = oracle.decode(case)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-3
+
+
+def test_decode_page_permutation_bitwise_invariant():
+    a = synth.make_decode_case(304, 2, 16, 2, seq_lens=[900, 333])
+    b = synth.make_decode_case(304, 2, 16, 2, seq_lens=[900, 333])
+    # same logical rows, new physical placement
+    c = b.cache
+    perm = np.random.default_rng(11).permutation(c.num_pages)
+    new_data = np.empty_like(c.data)
+    new_data[perm] = c.data
+    c.data = new_data
+    c.page_table = perm[c.page_table].astype(np.int32)
+    c.poison_page = int(perm[c.poison_page])
+    oa, la = run_decode(a)
+    ob, lb = run_decode(b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)) and torch.equal(la, lb)
+
+
+def test_decode_deterministic():
+    case = synth.make_decode_case(305, 4, 16, 4, seq_lens=[5000, 4000, 100, 2500])
+    d = decode_inputs(case)
+    o1, l1 = run_decode(case, d)
+    o2, l2 = run_decode(case, d)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_decode_nan_poison_has_no_effect():
+    """Tails past each length and unused page-table entries point at NaN rows: the output
+    must equal the run with finite poison bit for bit."""
+    lens = [70, 129, 1]
+    a = synth.make_decode_case(306, 3, 16, 1, seq_lens=lens, max_seq_len=400)
+    b = synth.make_decode_case(306, 3, 16, 1, seq_lens=lens, max_seq_len=400, poison=synth.POISON_NAN)
+    oa, la = run_decode(a)
+    ob, lb = run_decode(b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)) and torch.equal(la, lb)
+    assert torch.isfinite(ob.float()).all()
+
+
+def test_decode_short_workspace_is_rejected():
+    case = synth.make_decode_case(307, 4, 16, 4, seq_lens=[4096] * 4)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mla.MLAError) as e:
+        run_decode(case, workspace=ws)
+    assert e.value.status == mla.MLA_ERR_WORKSPACE
+
+
+def test_decode_workload1_sampled():
+    """Full-size 64K-row decode (4 requests x 4 drafts x 16 heads), as benchmarked;
+    the oracle evaluates one draft of each request, all heads."""
+    case = synth.make_workload(1)
+    out, lse = host(*run_decode(case))
+    toks = [0, 5, 10, 15]  # request b, draft b
+    ref_out, ref_lse = oracle.decode(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
+    errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, case.name)
+    print("workload1 sampled: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)
