@@ -1,0 +1,252 @@
+"""Benchmark: MLA decode HBM GB/s on the 64K-row speculative-decode workload,
+plus varlen-prefill TFLOP/s on the long-prefix prefill workload, one GPU.
+
+One step is one ``mla_decode`` call on workload ``decode_b4_h16_q4_L64K``
+(4 requests x 4 draft tokens x 16 heads against 65,536 cached latent rows
+each), i.e. the whole decode path: split plan, page-table walk, staged
+pages, both MFMA contractions, online softmax, partials and merge.  Inputs
+are resident in HBM before timing; consecutive steps rotate through three
+copies of the cache (906 MB > 3 x the 256 MB Infinity Cache), so each step
+reads its rows from HBM.  ``value`` is algorithmic bytes per step / step
+time: the cache rows every request holds, the query, the page-table entries
+and lengths read, and the output and LSE written (no split-KV workspace
+traffic, no re-reads).
+
+The prefill leg times ``mla_prefill_varlen`` on
+``prefill_b8_h16_P16K-96K_N200-2000`` and reports TFLOP/s of the absorbed
+form as called (2 * 1088 flops per visible (query row, cached row) pair).
+
+The CPU baseline is the fp64 oracle on the host's cores (at most 16
+threads), timed on the full decode workload (all 16 query tokens, all
+heads); it is a reported baseline, not a target.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
+                       [--no-cpu-baseline] [--prefill-steps P]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode HBM GB/s (% peak) + varlen prefill TFLOP/s, 64K-prefix KV, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FLOP_PER_PAIR = 2 * (576 + 512)
+
+
+def decode_algorithmic_bytes(case) -> int:
+    """Bytes the decode method itself must move (see module docstring)."""
+    c = case.cache
+    L = c.kv_lens.astype(np.int64)
+    row_bytes = 576 * 2 if c.kv_dtype == "bf16" else 576 + 4
+    T, H = case.total_q(), case.heads
+    pages = int(((L + 63) // 64).sum())
+    return int(L.sum() * row_bytes + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4 + pages * 4
+               + case.batch * 4)
+
+
+def decode_flops(case) -> int:
+    L = case.cache.kv_lens.astype(np.int64)
+    vis = 0
+    for b in range(case.batch):
+        for i in range(case.q_len):
+            vis += int(L[b]) - case.q_len + i + 1
+    return vis * case.heads * FLOP_PER_PAIR
+
+
+def prefill_flops(case) -> int:
+    tot = 0
+    for b in range(case.batch):
+        P = int(case.prefix_lens[b])
+        n = int(case.cu_seqlens_q[b + 1] - case.cu_seqlens_q[b])
+        tot += n * P + n * (n + 1) // 2
+    return tot * case.heads * FLOP_PER_PAIR
+
+
+def prefill_algorithmic_bytes(case) -> int:
+    c = case.cache
+    L = c.kv_lens.astype(np.int64)
+    T, H = case.total_q(), case.heads
+    return int(L.sum() * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4)
+
+
+def time_calls(fn_list, stream, warmup: int, steps: int):
+    """Run fn_list[i % len] warmup + steps times; events around every timed call on
+    `stream`.  Returns (total ms of the timed region, per-call ms list)."""
+    import torch
+    for i in range(warmup):
+        fn_list[i % len(fn_list)]()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for i in range(steps):
+            starts[i].record(stream)
+            fn_list[(warmup + i) % len(fn_list)]()
+            ends[i].record(stream)
+        t1.record(stream)
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return t0.elapsed_time(t1), per
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB (3 times), whose "
+                         "HBM counter readings calibrate the per-kernel FETCH_SIZE / WRITE_SIZE figures")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how the decode would shard). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mla_attention_paged_amd as mla
+    import synth
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from mla_gpu import decode_inputs, prefill_inputs
+
+    torch.cuda.set_device(0)
+    mla.library()
+    stream = torch.cuda.Stream()
+
+    # ---------------- decode: the metric ----------------
+    t_gen = time.time()
+    case = synth.make_workload(1)
+    gen_s = time.time() - t_gen
+    base = decode_inputs(case)
+    kv_copies = [base["kv"]] + [base["kv"].clone() for _ in range(max(0, args.copies - 1))]
+    T, H = case.total_q(), case.heads
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws_bytes = mla.mla_splitkv_workspace_size(case.batch, H, case.q_len, T, case.max_seq_len, base["kind"])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    grid, _ = mla.mla_decode_plan(case.batch, H, case.q_len, case.max_seq_len, base["kind"])
+
+    def make_call(kv):
+        def call():
+            mla.mla_decode(base["q"], kv, base["scale"], base["kind"], base["pt"], case.cache.max_pages,
+                           base["seq_lens"], case.batch, case.q_len, H, 64, case.max_seq_len,
+                           case.softmax_scale, out, lse, ws, ws.numel(), stream)
+        return call
+
+    calls = [make_call(kv) for kv in kv_copies]
+    total_ms, per = time_calls(calls, stream, args.warmup, args.steps)
+    ms_per_step = total_ms / args.steps
+    nbytes = decode_algorithmic_bytes(case)
+    flops = decode_flops(case)
+    call_ms = float(np.mean(per))
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "batch": case.batch, "heads": H, "q_len": case.q_len,
+                   "kv_len": int(case.seq_lens[0]), "page_size": 64, "kv_dtype": "bf16",
+                   "kv_copies_rotated": len(kv_copies), "phase1_workgroups": grid},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_decode call (decode_phase1 + decode_merge)",
+                     "algorithmic_bytes_per_call": nbytes,
+                     "us_per_call": {"mean": round(call_ms * 1e3, 2),
+                                     "p10": round(float(np.percentile(per, 10)) * 1e3, 2),
+                                     "p50": round(float(np.percentile(per, 50)) * 1e3, 2),
+                                     "p90": round(float(np.percentile(per, 90)) * 1e3, 2)}},
+        "decode_tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
+        "input_generation_s": round(gen_s, 1),
+    }
+
+    # ---------------- prefill leg ----------------
+    if not args.no_prefill:
+        pcase = synth.make_workload(3)
+        pin = prefill_inputs(pcase)
+        PT = pcase.total_q()
+        pout = torch.empty((PT, pcase.heads, 512), dtype=torch.bfloat16, device="cuda")
+        plse = torch.empty((PT, pcase.heads), dtype=torch.float32, device="cuda")
+        pws_bytes = mla.mla_splitkv_workspace_size(pcase.batch, pcase.heads, pcase.max_q_len(), PT,
+                                                   pcase.max_seq_len, pin["kind"])
+        pws = torch.empty(max(pws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+        def pcall():
+            mla.mla_prefill_varlen(pin["q"], pin["cu"], pin["prefix"], pin["kv"], pin["scale"], pin["kind"],
+                                   pin["pt"], pcase.cache.max_pages, pcase.batch, PT, pcase.max_q_len(),
+                                   pcase.max_seq_len, pcase.heads, 64, pcase.softmax_scale, pout, plse,
+                                   pws, pws.numel(), stream)
+
+        ptotal, pper = time_calls([pcall], stream, 2, args.prefill_steps)
+        pflops = prefill_flops(pcase)
+        pms = float(np.mean(pper))
+        tflops = pflops / (pms * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": pcase.name, "total_new_tokens": PT, "heads": pcase.heads,
+            "prefix_lens": pcase.prefix_lens.tolist(),
+            "new_lens": np.diff(pcase.cu_seqlens_q).tolist(),
+            "ms_per_call": round(pms, 3), "tflops": round(tflops, 2), "flops_per_call": pflops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
+        }
+
+    # ---------------- counter calibration: a plain copy of known size ----------------
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n
+        del src, dst
+
+    # ---------------- CPU baseline: the oracle ----------------
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = max(1, min(16, os.cpu_count() or 1))
+        t = time.time()
+        oracle.decode(case, nthreads=cores)
+        cpu_s = time.time() - t
+        result["cpu_baseline"] = {"value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": cores,
+                                  "kind": "oracle", "seconds": round(cpu_s, 2),
+                                  "sample": f"the full {case.name} call (all {T} query tokens x {H} heads), "
+                                            "fp64 C oracle, one run"}
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

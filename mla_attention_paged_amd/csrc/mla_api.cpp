@@ -27,7 +27,7 @@ DecodePlan plan_decode(int batch, int heads, int q_len, int max_seq_len, int kv_
   (void)kv_dtype;
   DecodePlan p{};
   const int rows = q_len * heads;
-  p.waves = rows > 64 ? 8 : 4;
+  p.waves = 8;
   // One phase-one workgroup per compute unit (each holds two 72 KB pages of
   // LDS), but at least 4 pages of work per workgroup.
   const long long pages_max = (long long)batch * ceil_div(max_seq_len, kPage);
@@ -57,12 +57,10 @@ PrefillPlan plan_prefill(int batch, int heads, int max_q_len, int total_q, int m
   (void)max_seq_len;
   (void)kv_dtype;
   PrefillPlan p{};
-  // A work tile is as many whole query tokens as fit in 64 rows (four
-  // waves of 16 rows); a token with more than 64 heads is one tile of up to
-  // 128 rows (eight waves).
+  // A work tile is as many whole query tokens as fit in one block of 64
+  // query rows; a token with more than 64 heads is one tile per 64-row block.
   p.tok_per_tile = heads >= 64 ? 1 : 64 / heads;
-  const int rows = p.tok_per_tile * heads;
-  p.waves = rows > 64 ? 8 : 4;
+  p.waves = 8;
   p.grid = num_cus > 0 ? num_cus : 1;
   size_t off = 0;
   p.counter_off = off;

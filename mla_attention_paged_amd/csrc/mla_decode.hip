@@ -53,35 +53,40 @@ __device__ __forceinline__ int owner_group(long long p, long long P, int G) {
 }
 
 // Write the rows of one finished (request, share) pair: the final output
-// when phase one is the only phase, else the partial in slot `slot`.
+// when phase one is the only phase, else the partial in slot `slot`.  Wave
+// half h writes value columns 256h .. 256h + 255; half 0 writes the LSE.
 __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& st, int b, int slot,
-                                           int row, bool row_ok, int lane) {
+                                           int row, bool row_ok, int half, int lane) {
   float inv, lse2;
   finish_row(st, inv, lse2);
   if (!row_ok) return;
   const int g = lane >> 4;
+  const int col0 = (kDv / 2) * half + 4 * g;
   if (a.grid == 1) {
-    uint16_t* dst = a.out + ((size_t)b * a.rows + row) * kDv + 4 * g;
+    uint16_t* dst = a.out + ((size_t)b * a.rows + row) * kDv + col0;
 #pragma unroll
-    for (int ct = 0; ct < kOFrags; ++ct) {
+    for (int ct = 0; ct < kOHalf; ++ct) {
       const f32x4 v = st.o[ct] * inv;
       bf16x4 h;
       h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
       *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
     }
-    if (g == 0) a.lse[(size_t)b * a.rows + row] = lse2 * kLn2;
+    if (g == 0 && half == 0) a.lse[(size_t)b * a.rows + row] = lse2 * kLn2;
   } else {
-    float* dst = a.part_o + ((size_t)slot * a.rows + row) * kDv + 4 * g;
+    float* dst = a.part_o + ((size_t)slot * a.rows + row) * kDv + col0;
 #pragma unroll
-    for (int ct = 0; ct < kOFrags; ++ct) *reinterpret_cast<f32x4*>(dst + 16 * ct) = st.o[ct] * inv;
-    if (g == 0) a.part_lse[(size_t)slot * a.rows + row] = lse2;
+    for (int ct = 0; ct < kOHalf; ++ct) *reinterpret_cast<f32x4*>(dst + 16 * ct) = st.o[ct] * inv;
+    if (g == 0 && half == 0) a.part_lse[(size_t)slot * a.rows + row] = lse2;
   }
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void decode_phase1(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[2 * kTileBytes];
-  MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)tiles_raw;
+// Phase one.  blockIdx.x: share of the page stream; blockIdx.y: block of 64
+// folded rows (requests with more than 64 rows use two).
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[kWaves * 64];
+  MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
+  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
   __shared__ int s_pid[kWin], s_req[kWin], s_rem[kWin];
   __shared__ int s_info[4];
 
@@ -93,14 +98,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_phase1(DecodeArgs a) {
   // ---- locate this workgroup's share of the page stream (wave 0) ----
   if (w == 0) {
     long long P = 0;
+    const bool write_cum = g == 0 && blockIdx.y == 0 && G > 1;
     for (int base = 0; base < a.batch; base += 64) {
       const int b = base + lane;
       const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
       const int incl = wave_incl_scan(np, lane);
-      if (g == 0 && G > 1 && b < a.batch) a.cum_pages[b] = (int)(P + incl - np);
+      if (write_cum && b < a.batch) a.cum_pages[b] = (int)(P + incl - np);
       P += __shfl(incl, 63);
     }
-    if (g == 0 && G > 1 && lane == 0) a.cum_pages[a.batch] = (int)P;
+    if (write_cum && lane == 0) a.cum_pages[a.batch] = (int)P;
     const long long lo = P * g / G, hi = P * (g + 1) / G;
     int b0 = a.batch, j0 = 0;
     if (lo < hi) {
@@ -133,12 +139,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_phase1(DecodeArgs a) {
   if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
   int cb = s_info[2], cj = s_info[3];
 
-  // ---- this wave's 16 query rows ----
-  const int row = 16 * w + (lane & 15);
-  const bool wave_rows = 16 * w < a.rows;
+  // ---- this wave's 16 query rows (shared with wave w ^ 4) ----
+  const int half = w >> 2;
+  const int row = kBlockRows * blockIdx.y + 16 * (w & 3) + (lane & 15);
+  const bool wave_rows = kBlockRows * blockIdx.y + 16 * (w & 3) < a.rows;
   const bool row_ok = row < a.rows;
   const int draft = row_ok ? row / a.heads : 0;  // token index i of this row within its request
   const int late = a.q_len - draft;              // row sees rows t <= L - late
+  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
+  const MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
 
   RowState st;
   bf16x8 qf[kQFrags];
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_phase1(DecodeArgs a) {
   for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
     const int n = min(kWin, seg_hi - wlo);
     __syncthreads();  // the previous window's list and stages are no longer read
-    for (int k = threadIdx.x; k < n; k += NW * 64) {
+    for (int k = threadIdx.x; k < n; k += kWaves * 64) {
       int b = cb, off = cj + k, Lc;
       for (;;) {
         Lc = clamp_len(a.seq_lens[b], a.max_pages);
@@ -174,36 +183,60 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_phase1(DecodeArgs a) {
     }
     __syncthreads();
 
-    stage_page<NW>(a.kv + (size_t)s_pid[0] * kPageBytes, tiles, min(kPage, s_rem[0]), w, lane);
-    for (int k = 0; k < n; ++k) {
-      const int b = s_req[k];
+    // Tiles are half pages: tile k is half (k & 1) of window page k >> 1.
+    // Three tiles are in flight while one is consumed.
+    const int ntiles = 2 * n;
+    auto issue = [&](int k) {
+      const int p = k >> 1;
+      stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, s_rem[p],
+                         ring + (k % kStages) * kStageBytes, w, lane);
+    };
+    const int pre = min(kStages - 1, ntiles);
+    for (int k = 0; k < pre; ++k) issue(k);
+    for (int k = 0; k < ntiles; ++k) {
+      const int p = k >> 1;
+      const int b = s_req[p];
+      const int rem = s_rem[p] - kTileRows * (k & 1);  // request rows from this tile's start
       if (b != cur_b) {
-        if (cur_b >= 0 && wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, lane);
+        if (cur_b >= 0 && wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
         cur_b = b;
         if (wave_rows) {
           load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
           reset_state(st);
         }
       }
-      const int rem = s_rem[k];
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of page k have landed in LDS
-      __syncthreads();                // ... and every other wave's; page k-1's stage is free
-      if (k + 1 < n)
-        stage_page<NW>(a.kv + (size_t)s_pid[k + 1] * kPageBytes, tiles + ((k + 1) & 1) * kTileBytes,
-                   min(kPage, s_rem[k + 1]), w, lane);
-      if (wave_rows) attend_page(tiles + (k & 1) * kTileBytes, qf, rem - late, a.scale_log2, lane, st);
+      wait_tile<kWaves>(min(kStages - 2, ntiles - 1 - k), w);  // this wave's loads of tile k landed
+      lds_barrier();                                           // ... every wave's; tile k-1's stage is free
+      if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
+      if (rem > 0) {  // uniform: every wave takes part in the exchange barrier
+        if (wave_rows)
+          attend_tile(ring + (k % kStages) * kStageBytes, qf, rem - late, a.scale_log2, lane, half, xmine,
+                      xpart, st);
+        else
+          lds_write_barrier();
+      }
     }
   }
-  if (wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, lane);
+  if (wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
 }
 
 // Phase two: per (request, row), reduce the partials of the workgroups
-// whose shares intersect the request.  One wave per row; lane owns 8
-// consecutive value columns.
+// whose shares intersect the request.  One workgroup per (row, half of the
+// value columns): a first pass takes the max partial log2-sum-exp, then wave
+// w accumulates shares w, w+4, ... (lane: 4 consecutive columns) and the
+// four waves are combined through LDS.
+__device__ __forceinline__ bool share_empty(long long P, int G, int gg) {
+  return P * gg / G >= P * (gg + 1) / G;
+}
+
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  __shared__ float s_red[4];
+  __shared__ float s_w[4];
+  __shared__ f32x4 s_acc[4][64];
   const int lane = threadIdx.x & 63;
-  const int R = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (R >= a.batch * a.rows) return;
+  const int w = threadIdx.x >> 6;
+  const int R = blockIdx.x;
+  const int half = blockIdx.y;
   const int b = R / a.rows, row = R - b * a.rows;
   const long long P = a.cum_pages[a.batch];
   const int G = a.grid;
@@ -212,42 +245,49 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int g0 = owner_group(p0, P, G), g1 = owner_group(p1 - 1, P, G);
 
   float m = -INFINITY;
-  for (int gg = g0; gg <= g1; ++gg) {
-    if (P * gg / G >= P * (gg + 1) / G) continue;  // empty share: wrote nothing
-    m = fmaxf(m, a.part_lse[(size_t)(gg + b) * a.rows + row]);
-  }
+  for (int gg = g0 + (int)threadIdx.x; gg <= g1; gg += 256)
+    if (!share_empty(P, G, gg)) m = fmaxf(m, a.part_lse[(size_t)(gg + b) * a.rows + row]);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+  if (lane == 0) s_red[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float m_use = m == -INFINITY ? 0.f : m;
+
   float wsum = 0.f;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int gg = g0; gg <= g1; ++gg) {
-    if (P * gg / G >= P * (gg + 1) / G) continue;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int col = half * (kDv / 2) + 4 * lane;
+#pragma unroll 4
+  for (int gg = g0 + w; gg <= g1; gg += 4) {
+    if (share_empty(P, G, gg)) continue;
     const size_t slot = (size_t)(gg + b) * a.rows + row;
     const float wgt = fast_exp2(a.part_lse[slot] - m_use);
     wsum += wgt;
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + slot * kDv + 8 * lane);
-    acc0 += src[0] * wgt;
-    acc1 += src[1] * wgt;
+    acc += *reinterpret_cast<const f32x4*>(a.part_o + slot * kDv + col) * wgt;
   }
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  acc0 *= inv;
-  acc1 *= inv;
-  bf16x8 h;
-  h[0] = (__bf16)acc0[0]; h[1] = (__bf16)acc0[1]; h[2] = (__bf16)acc0[2]; h[3] = (__bf16)acc0[3];
-  h[4] = (__bf16)acc1[0]; h[5] = (__bf16)acc1[1]; h[6] = (__bf16)acc1[2]; h[7] = (__bf16)acc1[3];
-  *reinterpret_cast<bf16x8*>(a.out + (size_t)R * kDv + 8 * lane) = h;
-  if (lane == 0) a.lse[R] = wsum > 0.f ? (m_use + fast_log2(wsum)) * kLn2 : -INFINITY;
+  s_acc[w][lane] = acc;
+  if (lane == 0) s_w[w] = wsum;
+  __syncthreads();
+  if (w == 0) {
+    const float tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    const f32x4 o = s_acc[0][lane] + s_acc[1][lane] + s_acc[2][lane] + s_acc[3][lane];
+    const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+    bf16x4 h;
+    h[0] = (__bf16)(o[0] * inv); h[1] = (__bf16)(o[1] * inv);
+    h[2] = (__bf16)(o[2] * inv); h[3] = (__bf16)(o[3] * inv);
+    *reinterpret_cast<bf16x4*>(a.out + (size_t)R * kDv + col) = h;
+    if (half == 0 && lane == 0) a.lse[R] = tot > 0.f ? (m_use + fast_log2(tot)) * kLn2 : -INFINITY;
+  }
 }
 
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream) {
   (void)kv_dtype;
-  if (plan.waves == 8)
-    hipLaunchKernelGGL(decode_phase1<8>, dim3(plan.grid), dim3(512), 0, stream, args);
-  else
-    hipLaunchKernelGGL(decode_phase1<4>, dim3(plan.grid), dim3(256), 0, stream, args);
+  const int row_blocks = (args.rows + kBlockRows - 1) / kBlockRows;
+  hipLaunchKernelGGL(decode_phase1, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.grid == 1) return e;
   const int total_rows = args.batch * args.rows;
-  hipLaunchKernelGGL(decode_merge, dim3((total_rows + 3) / 4), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL(decode_merge, dim3(total_rows, 2), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -1,30 +1,41 @@
 // Device building blocks shared by the decode and prefill kernels (gfx950).
 //
-// A workgroup stages one 64-row cache page at a time in LDS and every wave
-// attends its own 16 query rows against it:
+// A workgroup of eight waves (two per SIMD) attends a block of up to 64
+// query rows against the cache, which it streams through a ring of four
+// LDS stages of 32 cache rows (half a page) each: three tiles are in flight
+// while the fourth is consumed.  Waves w and w + 4 share the 16 query rows
+// 16 (w % 4) .. +15 and split the work of each tile in two halves, h = w / 4:
 //
-//   S^T = K * Q^T     v_mfma_f32_16x16x32_bf16, A = K rows from LDS
-//                     (16 tokens x 32 features per instruction), B = the
-//                     wave's Q rows held in registers for the whole call
-//   online softmax    in the S^T accumulator layout, each lane owns one
-//                     query row and 16 of the page's 64 tokens, so the row
-//                     max needs two cross-lane exchanges and the row sum
-//                     none (it is reduced once, at the end)
-//   O^T += V^T * P^T  A = V^T read with ds_read_b64_tr_b16 (the value
-//                     columns are the first 512 columns of the same staged
-//                     page), B = P^T taken straight from the S^T
-//                     accumulators, so P never goes through LDS
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over the 576 features: A = 16
+//                   cache rows (rows 16h .. 16h + 15 of the tile) read from
+//                   LDS, B = the wave's Q rows, held in registers for the
+//                   whole range
+//   exchange        each wave hands its 16 x 16 score block to its partner
+//                   through LDS, so both hold the row's scores for all 32
+//                   rows of the tile
+//   online softmax  identical in both waves: each lane owns one query row
+//                   and 8 of the 32 rows, so the row max needs two lane
+//                   swaps and the row sum none (it is reduced at the end)
+//   O^T += V^T P^T  A = V^T read with ds_read_b64_tr_b16 (the value columns
+//                   are the first 512 columns of the same staged rows), B =
+//                   P^T taken straight from the score registers; wave half h
+//                   accumulates value columns 256h .. 256h + 255
 //
-// The O^T accumulators give each lane one query row and 4 consecutive value
-// columns per 16-column tile, so the softmax rescale is a per-lane scalar.
+// Splitting the value columns halves the accumulators (64 registers), which
+// is what lets two waves share a SIMD and hide each other's softmax, LDS and
+// barrier latency behind their MFMAs; splitting the score rows keeps the
+// total MFMA and LDS work per tile the same as with one wave per 16 rows.
 //
-// LDS layout of a staged page: row t starts at byte t * 1168 (the 1152-byte
-// row plus one 16-byte pad).  The odd pitch (73 chunks) puts the 16 tokens
-// one A-operand read touches, and the 4 tokens x 16 columns one transposed
-// read touches, on distinct banks, while every LDS address stays an affine
-// function of the loop indices, so it folds into the instructions'
-// immediate offsets.  A page is exactly 73 wave-wide direct-to-LDS loads;
-// the lanes that land on a pad slot re-read chunk 0 of their row.
+// LDS layout of a staged tile: row t starts at byte t * 1184 (the 1152-byte
+// row plus 32 bytes of pad; 296 dwords, an odd multiple of 8 modulo the 64
+// banks).  Measured on gfx950, this pitch serves both read shapes near the
+// LDS peak: the A-operand reads of 16 rows x 16 bytes (~220 B/clk/CU) and
+// the transposed reads of 16 rows x 32 bytes (~145 B/clk/CU), against ~120
+// for a 1168-byte pitch and ~60 for the unpadded 1152.  Every LDS address
+// stays an affine function of the loop indices, so it folds into the
+// instructions' immediate offsets.  A tile is exactly 37 wave-wide
+// direct-to-LDS loads; the lanes that land on a pad slot re-read chunk 0 of
+// their row.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,13 +56,19 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRowBytes = kDqk * 2;            // 1152: one cache row in HBM
 constexpr int kRowChunks = kRowBytes / 16;     // 72
 constexpr int kPageBytes = kPage * kRowBytes;  // 73728: one page in HBM
-constexpr int kLdsPitch = kRowBytes + 16;      // 1168: one row in LDS
-constexpr int kLdsChunks = kLdsPitch / 16;     // 73
-constexpr int kTileBytes = kPage * kLdsPitch;  // 74752: one staged page in LDS
-constexpr int kTileLoads = kTileBytes / 1024;  // 73 wave-wide 16-byte loads per page
-static_assert(kTileLoads * 1024 == kTileBytes, "a staged page is a whole number of wave loads");
+constexpr int kLdsPitch = kRowBytes + 32;      // 1184: one row in LDS
+constexpr int kLdsChunks = kLdsPitch / 16;     // 74
+constexpr int kTileRows = 32;                  // rows per LDS stage (half a page)
+constexpr int kTileSlots = kTileRows * kLdsChunks;      // 2368 16-byte slots
+constexpr int kStageLoads = kTileSlots / 64;            // 37 wave-wide loads per tile
+static_assert(kStageLoads * 64 == kTileSlots, "a tile is a whole number of wave-wide loads");
+constexpr int kStageBytes = kStageLoads * 1024;         // 37888
+constexpr int kStages = 4;                     // ring depth: 3 tiles in flight
 constexpr int kQFrags = kDqk / 32;             // 18 k-steps of 32 features
 constexpr int kOFrags = kDv / 16;              // 32 value-column tiles
+constexpr int kWaves = 8;                      // waves per workgroup (two per SIMD)
+constexpr int kBlockRows = 64;                 // query rows per workgroup
+constexpr int kOHalf = kOFrags / 2;            // value-column tiles per wave
 
 // Byte offset of 16-byte chunk `chunk` of token `t` inside a staged page.
 __device__ __forceinline__ int tile_off(int t, int chunk) { return t * kLdsPitch + chunk * 16; }
@@ -60,65 +77,127 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-__device__ __forceinline__ float wave_max_rows(float v) {
-  // Max over the four lanes that hold the same query row (lane, lane^16, lane^32, lane^48).
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left free), GFX9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-__device__ __forceinline__ float wave_sum_rows(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
-
-// Global byte offset (within its page) that the lane's slot of wave-wide
-// load i must fetch.  Rows at or past `valid` re-read row 0 of the same
-// page, so the staged rows are always finite cache data and nothing past a
-// request's length is ever read.
-__device__ __forceinline__ int stage_src(int i, int lane, int valid) {
-  const int s = i * 64 + lane;              // 16-byte slot in the staged page
-  const int t = s / kLdsChunks;
-  int c = s - t * kLdsChunks;
-  c = c == kRowChunks ? 0 : c;              // pad slot
-  const int ts = t < valid ? t : 0;
-  return ts * kRowBytes + c * 16;
-}
-
-// Issue this wave's share (loads w, w + nwaves, ...) of the direct-to-LDS
-// loads of one cache page into `stage`.
+// Direct-to-LDS loads wave w issues per tile.
 template <int NW>
-__device__ __forceinline__ void stage_page(const uint8_t* __restrict__ page, MLA_LDS uint8_t* stage,
-                                           int valid, int wave, int lane) {
-  if (valid >= kPage) {
-#pragma unroll
-    for (int i0 = 0; i0 < kTileLoads; i0 += NW) {
-      const int i = i0 + wave;
-      if (NW * ((kTileLoads + NW - 1) / NW) == kTileLoads || i < kTileLoads)
-        __builtin_amdgcn_global_load_lds((const void*)(page + stage_src(i, lane, kPage)),
-                                         (MLA_LDS void*)(stage + i * 1024), 16, 0, 0);
-    }
+__device__ __forceinline__ constexpr int stage_loads_of(int w) { return (kStageLoads - w + NW - 1) / NW; }
+
+// Wait until this wave's loads of the oldest outstanding tile have landed,
+// leaving the loads of `ahead` (0..2) younger tiles in flight.
+template <int NW>
+__device__ __forceinline__ void wait_tile(int ahead, int w) {
+  constexpr int hi = stage_loads_of<NW>(0);
+  constexpr int lo = stage_loads_of<NW>(NW - 1);
+  const bool big = stage_loads_of<NW>(w) == hi;
+  if (ahead >= 2) {
+    if (big) wait_vmcnt<2 * hi>(); else wait_vmcnt<2 * lo>();
+  } else if (ahead == 1) {
+    if (big) wait_vmcnt<hi>(); else wait_vmcnt<lo>();
   } else {
-    for (int i = wave; i < kTileLoads; i += NW)
-      __builtin_amdgcn_global_load_lds((const void*)(page + stage_src(i, lane, valid)),
-                                       (MLA_LDS void*)(stage + i * 1024), 16, 0, 0);
+    wait_vmcnt<0>();
   }
 }
 
-// Per-wave attention state: 16 query rows, one per lane group position.
+// Workgroup barrier that is also a compiler memory barrier, without the
+// vmcnt(0) that a full fence would add (it would drain the load ring).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Same, after this wave's own LDS writes have completed.
+__device__ __forceinline__ void lds_write_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Reductions over the four lanes that hold the same query row (lane,
+// lane^16, lane^32, lane^48), with the gfx950 row-swap permutes (VALU only,
+// no LDS round trip).  Each swap returns the lane's own value and its
+// partner's in some order; max and sum of the pair are symmetric, so the
+// result is the same whichever output holds which, and it is bitwise equal
+// on all four lanes.
+__device__ __forceinline__ float pair_max(float v, bool x32) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = x32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float v, bool x32) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = x32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_max_rows(float v) { return pair_max(pair_max(v, false), true); }
+__device__ __forceinline__ float wave_sum_rows(float v) { return pair_sum(pair_sum(v, false), true); }
+
+// Global byte offset (within its page) that the lane's slot of wave-wide
+// load i of tile `half` (0: rows 0-31 of the page, 1: rows 32-63) fetches.
+// Rows at or past `rem` (the request's rows from the page start) re-read row
+// 0 of the page, so the staged rows are always finite cache data and nothing
+// past a request's length is ever read.
+__device__ __forceinline__ int stage_src(int i, int lane, int half, int rem) {
+  const int s = i * 64 + lane;              // 16-byte slot in the stage
+  const int t = s / kLdsChunks;             // 0..31
+  int c = s - t * kLdsChunks;
+  c = c >= kRowChunks ? 0 : c;              // pad slots
+  const int row = kTileRows * half + t;
+  const int src = row < rem ? row : 0;
+  return src * kRowBytes + c * 16;
+}
+
+// One wave-wide direct-to-LDS load: lane l's 16 bytes at base + voff land at
+// LDS byte lds + 16 l.  Issued as inline assembly so that the compiler does
+// not track it: its alias analysis cannot tell ring stages apart and would
+// otherwise wait for every in-flight stage before each LDS read.  The
+// kernels synchronise the ring themselves (wait_tile + s_barrier).  M0 holds
+// the LDS address; the s_nop covers the M0-write hazard.
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, int voff, const MLA_LDS uint8_t* lds) {
+  // Both scalar operands are wave-uniform; readfirstlane makes that explicit
+  // so that they are allocated to SGPRs.
+  // (readfirstlane returns int: go through uint32_t so that neither half is
+  // sign-extended when the 64-bit address is reassembled)
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t bs = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m), "v"(voff), "s"(bs)
+               : "memory");
+}
+
+// Issue this wave's share (loads w, w + NW, ...) of the direct-to-LDS loads
+// of one tile into `stage`.
+template <int NW>
+__device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ page, int half, int rem,
+                                           MLA_LDS uint8_t* stage, int wave, int lane) {
+#pragma unroll
+  for (int i0 = 0; i0 < kStageLoads; i0 += NW) {
+    const int i = i0 + wave;
+    if (i < kStageLoads) lds_dma16(page, stage_src(i, lane, half, rem), stage + i * 1024);
+  }
+}
+
+// Per-wave attention state: 16 query rows x 256 value columns.
 struct RowState {
-  f32x4 o[kOFrags];  // O^T: lane holds row (lane & 15), columns 16*ct + 4*(lane>>4) + e
+  f32x4 o[kOHalf];   // O^T: lane holds row (lane & 15), columns 256h + 16ct + 4(lane>>4) + e
   float m;           // running max of scaled scores, log2 units (row-uniform)
   float l;           // this lane's share of the running sum
 };
 
 __device__ __forceinline__ void reset_state(RowState& st) {
 #pragma unroll
-  for (int i = 0; i < kOFrags; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kOHalf; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
 }
@@ -137,6 +216,9 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, int la
 #pragma unroll
     for (int ks = 0; ks < kQFrags; ++ks) qf[ks] = bf16x8{};
   }
+  // Settle the Q loads here: otherwise the tile loop, whose in-flight load
+  // count the compiler cannot track, would wait for every load before each tile.
+  wait_vmcnt<0>();
 }
 
 // Scores may run this far (log2 units) above the running max before the
@@ -154,62 +236,78 @@ __device__ __forceinline__ bf16x4 lds_tr16(const MLA_LDS uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p));
 }
 
-// Attend one staged page.  Token tt of the page is visible to this lane's
-// row when tt <= lim (lim >= 63: whole page visible).
-__device__ __forceinline__ void attend_page(const MLA_LDS uint8_t* tile, const bf16x8 (&qf)[kQFrags],
-                                            int lim, float scale_log2, int lane, RowState& st) {
+// LDS read prefetch distances (in MFMA steps) of the two contractions.
+constexpr int kKDepth = 3;
+constexpr int kVDepth = 3;
+
+// Attend one staged tile of 32 rows (see the top of this file).  Token tt of
+// the tile is visible to this lane's row when tt <= lim (lim >= 31: all).
+// `half` is w / 4; xmine / xpart are this wave's and its partner's 1 KB
+// exchange slots.
+__device__ __forceinline__ void attend_tile(const MLA_LDS uint8_t* tile, const bf16x8 (&qf)[kQFrags],
+                                            int lim, float scale_log2, int lane, int half,
+                                            MLA_LDS f32x4* xmine, const MLA_LDS f32x4* xpart,
+                                            RowState& st) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  // ---- S^T = K Q^T for the page's 64 tokens (4 tiles of 16 tokens) ----
-  // K fragments of k-step ks+1 are read while the MFMAs of k-step ks run.
-  f32x4 acc[4];
-  bf16x8 kc[4], kn[4];
+  // ---- S^T = K Q^T for this wave's 16 rows of the tile ----
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 kb[kKDepth + 1];
+  const MLA_LDS uint8_t* kbase = tile + tile_off(16 * half + r16, g);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    kc[mt] = lds_b128(tile + tile_off(16 * mt + r16, g));  // k-step 0
-  }
+  for (int d = 0; d < kKDepth; ++d) kb[d] = lds_b128(kbase + 64 * d);
 #pragma unroll
   for (int ks = 0; ks < kQFrags; ++ks) {
-    if (ks + 1 < kQFrags) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) kn[mt] = lds_b128(tile + tile_off(16 * mt + r16, 4 * (ks + 1) + g));
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16x16x32(kc[mt], qf[ks], acc[mt]);
-    if (ks + 1 < kQFrags) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) kc[mt] = kn[mt];
-    }
+    if (ks + kKDepth < kQFrags) kb[(ks + kKDepth) % (kKDepth + 1)] = lds_b128(kbase + 64 * (ks + kKDepth));
+    acc = mfma16x16x32(kb[ks % (kKDepth + 1)], qf[ks], acc);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- scale, mask, online softmax ----
-  float s[16];
+  // ---- swap score blocks with the partner wave ----
+  *xmine = acc;
+  lds_write_barrier();
+  const f32x4 other = *xpart;
+  const f32x4 lo = half == 0 ? acc : other;  // tile rows 4g + e
+  const f32x4 hi = half == 0 ? other : acc;  // tile rows 16 + 4g + e
+
+  // First value fragments: requested now, consumed after the softmax.
+  // Transposed reads: lane i of its 16-lane group supplies row 4g + i/4 (and
+  // that + 16) and columns 256h + 16ct + 4(i%4) .. +3, and receives the 4
+  // rows of column 256h + 16ct + i.
+  const int i16 = lane & 15;
+  const int colq = 4 * (i16 & 3);
+  const int tq = 4 * g + (i16 >> 2);
+  const MLA_LDS uint8_t* vbase = tile + tq * kLdsPitch + colq * 2 + 512 * half;
+  bf16x4 vb[kVDepth + 1][2];
+#pragma unroll
+  for (int d = 0; d < kVDepth; ++d) {
+    vb[d][0] = lds_tr16(vbase + 32 * d);
+    vb[d][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * d);
+  }
+
+  // ---- scale, mask, online softmax (bitwise identical in both waves) ----
+  float s[8];
   float mx = -INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tt = 16 * mt + 4 * g + e;
-      float v = acc[mt][e] * scale_log2;
-      v = tt <= lim ? v : -INFINITY;
-      s[4 * mt + e] = v;
-      mx = fmaxf(mx, v);
-    }
+  for (int e = 0; e < 4; ++e) {
+    float v0 = lo[e] * scale_log2, v1 = hi[e] * scale_log2;
+    v0 = 4 * g + e <= lim ? v0 : -INFINITY;
+    v1 = 16 + 4 * g + e <= lim ? v1 : -INFINITY;
+    s[e] = v0;
+    s[4 + e] = v1;
+    mx = fmaxf(mx, fmaxf(v0, v1));
   }
   mx = wave_max_rows(mx);
-  // Raise the max only when the page's max exceeds it by more than the slack.
+  // Raise the max only when the tile's max exceeds it by more than the slack.
   const bool raise = mx > st.m + kRescaleSlack;
   if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
     const float m_new = raise ? mx : st.m;
     const float alpha = fast_exp2(st.m - m_new);  // st.m = -inf: 0; unchanged rows: 1
     st.m = m_new;
     st.l *= alpha;
-    // in groups, so that only a few accumulators are out of their registers at a time
 #pragma unroll
-    for (int c0 = 0; c0 < kOFrags; c0 += 4) {
+    for (int c0 = 0; c0 < kOHalf; c0 += 4) {
 #pragma unroll
       for (int ct = c0; ct < c0 + 4; ++ct) st.o[ct] *= alpha;
       __builtin_amdgcn_sched_barrier(0);
@@ -218,52 +316,28 @@ __device__ __forceinline__ void attend_page(const MLA_LDS uint8_t* tile, const b
   const float m_use = st.m == -INFINITY ? 0.f : st.m;
   float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     s[i] = fast_exp2(s[i] - m_use);
     psum += s[i];
   }
   st.l += psum;
-  bf16x8 pb[2];
+  bf16x8 pb;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pb[kk][e] = (__bf16)s[4 * (2 * kk) + e];
-      pb[kk][4 + e] = (__bf16)s[4 * (2 * kk + 1) + e];
-    }
-  }
+  for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- O^T += V^T P^T: 2 k-steps of 32 tokens x 32 column tiles ----
-  // Transposed reads: lane i of its 16-lane group supplies token
-  // 32kk + 4g + i/4 (and that + 16) and columns 16ct + 4(i%4) .. +3, and
-  // receives the 4 tokens of column 16ct + i.  Reads of step n+1 are issued
-  // while the MFMA of step n runs.
-  const int i16 = lane & 15;
-  const int colq = 4 * (i16 & 3);
-  const int tq = 4 * g + (i16 >> 2);
-  const MLA_LDS uint8_t* vbase = tile + tq * kLdsPitch + colq * 2;
-  auto v_addr = [&](int kk, int ct, int half) {
-    return vbase + (32 * kk + 16 * half) * kLdsPitch + 32 * ct;
-  };
-  bf16x4 va0 = lds_tr16(v_addr(0, 0, 0)), va1 = lds_tr16(v_addr(0, 0, 1));
+  // ---- O^T += V^T P^T: 32 rows x this wave's 16 column tiles ----
 #pragma unroll
-  for (int step = 0; step < 2 * kOFrags; ++step) {
-    const int kk = step / kOFrags, ct = step % kOFrags;
-    bf16x4 vn0, vn1;
-    if (step + 1 < 2 * kOFrags) {
-      const int kk1 = (step + 1) / kOFrags, ct1 = (step + 1) % kOFrags;
-      vn0 = lds_tr16(v_addr(kk1, ct1, 0));
-      vn1 = lds_tr16(v_addr(kk1, ct1, 1));
+  for (int ct = 0; ct < kOHalf; ++ct) {
+    if (ct + kVDepth < kOHalf) {
+      vb[(ct + kVDepth) % (kVDepth + 1)][0] = lds_tr16(vbase + 32 * (ct + kVDepth));
+      vb[(ct + kVDepth) % (kVDepth + 1)][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * (ct + kVDepth));
     }
+    const bf16x4 v0 = vb[ct % (kVDepth + 1)][0], v1 = vb[ct % (kVDepth + 1)][1];
     bf16x8 va;
-    va[0] = va0[0]; va[1] = va0[1]; va[2] = va0[2]; va[3] = va0[3];
-    va[4] = va1[0]; va[5] = va1[1]; va[6] = va1[2]; va[7] = va1[3];
-    st.o[ct] = mfma16x16x32(va, pb[kk], st.o[ct]);
-    if (step + 1 < 2 * kOFrags) {
-      va0 = vn0;
-      va1 = vn1;
-    }
+    va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
+    va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
+    st.o[ct] = mfma16x16x32(va, pb, st.o[ct]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }

@@ -9,8 +9,8 @@
 //          prefill kernel balances the scheduling across compute units.
 //
 // Work decomposition.  A work tile is up to `tok_per_tile` consecutive new
-// tokens of one request (tok_per_tile * heads <= 128 query rows, one wave per
-// 16 rows).  Its cost is proportional to the cached rows its last token sees
+// tokens of one request and one block of at most 64 of their query rows
+// (tok_per_tile * heads <= 64, or one token whose heads fill two blocks).  Its cost is proportional to the cached rows its last token sees
 // (prefix + position + 1).  A one-workgroup kernel orders the requests by the
 // cost of their most expensive tile, most expensive first, and lays out the
 // cumulative tile counts in that order; the tiles of a request are handed out
@@ -60,7 +60,8 @@ __global__ __launch_bounds__(256) void prefill_worklist(PrefillArgs a) {
       if (k < a.batch) {
         const int b = a.order[k];
         const int n = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
-        nt = n > 0 ? (n + a.tok_per_tile - 1) / a.tok_per_tile : 0;
+        const int row_blocks = (a.tok_per_tile * a.heads + 63) / 64;
+        nt = n > 0 ? (n + a.tok_per_tile - 1) / a.tok_per_tile * row_blocks : 0;
       }
       int incl = nt;
 #pragma unroll
@@ -75,21 +76,22 @@ __global__ __launch_bounds__(256) void prefill_worklist(PrefillArgs a) {
   }
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_persistent(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles_raw[2 * kTileBytes];
-  MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)tiles_raw;
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[kWaves * 64];
+  MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
+  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
   __shared__ int s_pid[kPWin];
   __shared__ int s_tile;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int half = w >> 2;
   const int total_tiles = a.tile_cum[a.batch];
-  const int rows_per_tile = a.tok_per_tile * a.heads;
-  const int row = 16 * w + (lane & 15);
-  const bool wave_rows = 16 * w < rows_per_tile;
-  const int tok_in_tile = row / a.heads;  // may exceed the tile's token count (then masked off)
-  const int head = row - tok_in_tile * a.heads;
+  const int block_rows = a.tok_per_tile * a.heads;                 // query rows of a token tile
+  const int row_blocks = (block_rows + kBlockRows - 1) / kBlockRows;
+  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
+  const MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
 
   RowState st;
   bf16x8 qf[kQFrags];
@@ -110,19 +112,26 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_persistent(PrefillArgs a) 
     const int b = a.order[lo];
     const int q0 = a.cu_seqlens[b];
     const int n_b = a.cu_seqlens[b + 1] - q0;
-    const int ntiles = (n_b + a.tok_per_tile - 1) / a.tok_per_tile;
-    const int jt = ntiles - 1 - (t - a.tile_cum[lo]);  // last tiles first
-    const int j0 = jt * a.tok_per_tile;                 // first new token of the tile
-    const int j1 = min(n_b, j0 + a.tok_per_tile);       // one past its last
+    const int ntok = (n_b + a.tok_per_tile - 1) / a.tok_per_tile;
+    const int local = t - a.tile_cum[lo];
+    const int jt = ntok - 1 - local / row_blocks;                  // last token tiles first
+    const int rb = local - (local / row_blocks) * row_blocks;      // row block
+    const int j0 = jt * a.tok_per_tile;                            // first new token of the tile
+    const int j1 = min(n_b, j0 + a.tok_per_tile);                  // one past its last
     const int P_b = a.prefix_lens[b];
     const int L_b = p_clamp(P_b + n_b, a.max_pages);
-    const int kv_end = min(L_b, P_b + j1);              // rows the tile's last token sees
+    const int kv_end = min(L_b, P_b + j1);                         // rows the tile's last token sees
     const int npages = (kv_end + kPage - 1) / kPage;
 
-    const int j = j0 + tok_in_tile;                     // this lane's new-token index
-    const bool row_ok = wave_rows && tok_in_tile < a.tok_per_tile && j < j1;
+    // this wave's 16 rows: row r of the tile is head r % heads of token j0 + r / heads
+    const int r = kBlockRows * rb + 16 * (w & 3) + (lane & 15);
+    const bool wave_rows = kBlockRows * rb + 16 * (w & 3) < block_rows;
+    const int tok_in_tile = r / a.heads;
+    const int head = r - tok_in_tile * a.heads;
+    const int j = j0 + tok_in_tile;                                // this lane's new-token index
+    const bool row_ok = wave_rows && r < block_rows && j < j1;
     const int tok = q0 + j;
-    const int vis_last = P_b + j;                       // last visible row of this query token
+    const int vis_last = P_b + j;                                  // last visible row of this query token
     if (wave_rows) {
       load_q(row_ok ? a.q + ((size_t)tok * a.heads + head) * kDqk : nullptr, lane, qf);
       reset_state(st);
@@ -131,20 +140,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_persistent(PrefillArgs a) 
     for (int plo = 0; plo < npages; plo += kPWin) {
       const int n = min(kPWin, npages - plo);
       __syncthreads();
-      for (int k = threadIdx.x; k < n; k += NW * 64)
+      for (int k = threadIdx.x; k < n; k += kWaves * 64)
         s_pid[k] = a.page_table[(size_t)b * a.max_pages + plo + k];
       __syncthreads();
-      stage_page<NW>(a.kv + (size_t)s_pid[0] * kPageBytes, tiles, min(kPage, kv_end - kPage * plo), w, lane);
-      for (int k = 0; k < n; ++k) {
-        const int pg = plo + k;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (k + 1 < n)
-          stage_page<NW>(a.kv + (size_t)s_pid[k + 1] * kPageBytes, tiles + ((k + 1) & 1) * kTileBytes,
-                     min(kPage, kv_end - kPage * (pg + 1)), w, lane);
+      // tiles of 32 rows: only those holding a row the tile's last token sees
+      const int ntiles = min(2 * n, (kv_end - kPage * plo + kTileRows - 1) / kTileRows);
+      auto issue = [&](int k) {
+        const int p = k >> 1;
+        stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, kv_end - kPage * (plo + p),
+                           ring + (k % kStages) * kStageBytes, w, lane);
+      };
+      const int pre = min(kStages - 1, ntiles);
+      for (int k = 0; k < pre; ++k) issue(k);
+      for (int k = 0; k < ntiles; ++k) {
+        const int t0 = kPage * plo + kTileRows * k;  // first cache row of tile k
+        wait_tile<kWaves>(min(kStages - 2, ntiles - 1 - k), w);
+        lds_barrier();
+        if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
         if (wave_rows) {
-          const int lim = row_ok ? vis_last - kPage * pg : -1;
-          attend_page(tiles + (k & 1) * kTileBytes, qf, lim, a.scale_log2, lane, st);
+          const int lim = row_ok ? vis_last - t0 : -1;
+          attend_tile(ring + (k % kStages) * kStageBytes, qf, lim, a.scale_log2, lane, half, xmine, xpart, st);
+        } else {
+          lds_write_barrier();  // the exchange barrier inside attend_tile
         }
       }
     }
@@ -154,15 +171,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_persistent(PrefillArgs a) 
       finish_row(st, inv, lse2);
       if (row_ok) {
         const int g = lane >> 4;
-        uint16_t* dst = a.out + ((size_t)tok * a.heads + head) * kDv + 4 * g;
+        uint16_t* dst = a.out + ((size_t)tok * a.heads + head) * kDv + (kDv / 2) * half + 4 * g;
 #pragma unroll
-        for (int ct = 0; ct < kOFrags; ++ct) {
+        for (int ct = 0; ct < kOHalf; ++ct) {
           const f32x4 v = st.o[ct] * inv;
           bf16x4 h;
           h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
           *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
         }
-        if (g == 0) a.lse[(size_t)tok * a.heads + head] = lse2 * kLn2;
+        if (g == 0 && half == 0) a.lse[(size_t)tok * a.heads + head] = lse2 * kLn2;
       }
     }
   }
@@ -173,10 +190,7 @@ hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int 
   hipLaunchKernelGGL(prefill_worklist, dim3(1), dim3(256), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (plan.waves == 8)
-    hipLaunchKernelGGL(prefill_persistent<8>, dim3(plan.grid), dim3(512), 0, stream, args);
-  else
-    hipLaunchKernelGGL(prefill_persistent<4>, dim3(plan.grid), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL(prefill_persistent, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -54,6 +54,8 @@ SMALL = [
     (107, 5, 16, 4, [4, 5, 63, 64, 127]),
     (108, 2, 64, 1, [700, 90]),
     (109, 1, 1, 1, [333]),
+    (110, 2, 32, 3, [500, 77]),      # 96 folded rows: eight waves
+    (111, 1, 128, 1, [1000]),        # 128 folded rows
 ]
 
 
