@@ -211,7 +211,6 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
   if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)batch * q_len * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_INVALID;
-  if (kv_dtype == MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;  // int8 kernels: not built yet
 
   DecodePlan plan{};
   const int rc = cached_decode_plan(batch, num_heads, q_len, max_seq_len, kv_dtype, &plan);
@@ -264,7 +263,6 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
   if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)total_q * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_INVALID;
-  if (kv_dtype == MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;  // int8 kernels: not built yet
   if (total_q == 0) return MLA_OK;
 
   int dev = 0, cus = 0;

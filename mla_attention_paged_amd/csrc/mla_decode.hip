@@ -81,11 +81,16 @@ __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& 
 }
 
 // Phase one.  blockIdx.x: share of the page stream; blockIdx.y: block of 64
-// folded rows (requests with more than 64 rows use two).
+// folded rows (requests with more than 64 rows use two).  I8: INT8 cache,
+// staged as codes + row scales and converted to exact bf16 per tile.
+template <bool I8>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[kStages * kStageBytes];
+  using R = Ring<I8>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[R::stages * R::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[I8 ? kStageBytes : 16];
   __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[kWaves * 64];
   MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
+  MLA_LDS uint8_t* const cvt = (MLA_LDS uint8_t*)cvt_raw;
   MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
   __shared__ int s_pid[kWin], s_req[kWin], s_rem[kWin];
   __shared__ int s_info[4];
@@ -184,14 +189,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
     __syncthreads();
 
     // Tiles are half pages: tile k is half (k & 1) of window page k >> 1.
-    // Three tiles are in flight while one is consumed.
+    // R::stages - 1 tiles are in flight while one is consumed.
     const int ntiles = 2 * n;
     auto issue = [&](int k) {
       const int p = k >> 1;
-      stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, s_rem[p],
-                         ring + (k % kStages) * kStageBytes, w, lane);
+      MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
+      if (I8)
+        stage_tile_i8<kWaves>(a.kv + (size_t)s_pid[p] * kI8PageBytes, a.kv_scale + (size_t)s_pid[p] * kPage,
+                              k & 1, s_rem[p], stage, w, lane);
+      else
+        stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, s_rem[p], stage, w, lane);
     };
-    const int pre = min(kStages - 1, ntiles);
+    const int pre = min(R::stages - 1, ntiles);
     for (int k = 0; k < pre; ++k) issue(k);
     for (int k = 0; k < ntiles; ++k) {
       const int p = k >> 1;
@@ -205,13 +214,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
           reset_state(st);
         }
       }
-      wait_tile<kWaves>(min(kStages - 2, ntiles - 1 - k), w);  // this wave's loads of tile k landed
-      lds_barrier();                                           // ... every wave's; tile k-1's stage is free
-      if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
-      if (rem > 0) {  // uniform: every wave takes part in the exchange barrier
+      wait_tile<kWaves, R::loads>(min(R::stages - 2, ntiles - 1 - k), w);  // this wave's loads of tile k landed
+      lds_barrier();  // ... every wave's; tile k-1's stage (and the converted tile) is free
+      if (k + R::stages - 1 < ntiles) issue(k + R::stages - 1);
+      if (rem > 0) {  // uniform: every wave takes part in the barriers below
+        const MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
+        const MLA_LDS uint8_t* tile = stage;
+        if (I8) {
+          convert_i8_tile(stage, cvt, threadIdx.x, kWaves * 64);
+          lds_write_barrier();
+          tile = cvt;
+        }
         if (wave_rows)
-          attend_tile(ring + (k % kStages) * kStageBytes, qf, rem - late, a.scale_log2, lane, half, xmine,
-                      xpart, st);
+          attend_tile<I8>(tile, qf, rem - late, a.scale_log2, lane, half, xmine, xpart, st,
+                          reinterpret_cast<const MLA_LDS float*>(stage + kI8CodeBytes));
         else
           lds_write_barrier();
       }
@@ -281,9 +297,11 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream) {
-  (void)kv_dtype;
   const int row_blocks = (args.rows + kBlockRows - 1) / kBlockRows;
-  hipLaunchKernelGGL(decode_phase1, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
+  if (kv_dtype == 1)
+    hipLaunchKernelGGL(decode_phase1<true>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
+  else
+    hipLaunchKernelGGL(decode_phase1<false>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.grid == 1) return e;
   const int total_rows = args.batch * args.rows;

@@ -64,6 +64,27 @@ constexpr int kStageLoads = kTileSlots / 64;            // 37 wave-wide loads pe
 static_assert(kStageLoads * 64 == kTileSlots, "a tile is a whole number of wave-wide loads");
 constexpr int kStageBytes = kStageLoads * 1024;         // 37888
 constexpr int kStages = 4;                     // ring depth: 3 tiles in flight
+
+// INT8 cache: a stage holds the 32 rows' codes (576 B each, unpadded: they
+// are only read by the conversion pass, 16 contiguous bytes per lane) and
+// their 32 fp32 scales.  Codes are half the bytes of a bf16 row, so the ring
+// is deeper (five tiles in flight) to keep as many bytes in flight.
+constexpr int kI8RowBytes = kDqk;                          // 576
+constexpr int kI8PageBytes = kPage * kI8RowBytes;          // 36864
+constexpr int kI8CodeBytes = kTileRows * kI8RowBytes;      // 18432: 18 wave-wide loads
+constexpr int kI8CodeLoads = kI8CodeBytes / 1024;
+constexpr int kI8StageLoads = kI8CodeLoads + 1;            // + one 8-lane load of the scales
+constexpr int kI8StageBytes = kI8CodeBytes + kTileRows * 4;  // 18560
+constexpr int kI8Stages = 6;
+
+// Ring geometry of each cache type.
+template <bool I8>
+struct Ring {
+  static constexpr int loads = I8 ? kI8StageLoads : kStageLoads;
+  static constexpr int stage_bytes = I8 ? kI8StageBytes : kStageBytes;
+  static constexpr int stages = I8 ? kI8Stages : kStages;
+  static constexpr int page_bytes = I8 ? kI8PageBytes : kPageBytes;
+};
 constexpr int kQFrags = kDqk / 32;             // 18 k-steps of 32 features
 constexpr int kOFrags = kDv / 16;              // 32 value-column tiles
 constexpr int kWaves = 8;                      // waves per workgroup (two per SIMD)
@@ -84,23 +105,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-// Direct-to-LDS loads wave w issues per tile.
-template <int NW>
-__device__ __forceinline__ constexpr int stage_loads_of(int w) { return (kStageLoads - w + NW - 1) / NW; }
+// Direct-to-LDS loads wave w issues per tile when LOADS are spread over NW
+// waves (load i is issued by wave i % NW).
+template <int NW, int LOADS = kStageLoads>
+__device__ __forceinline__ constexpr int stage_loads_of(int w) { return (LOADS - w + NW - 1) / NW; }
 
 // Wait until this wave's loads of the oldest outstanding tile have landed,
-// leaving the loads of `ahead` (0..2) younger tiles in flight.
-template <int NW>
+// leaving the loads of `ahead` (0..4) younger tiles in flight.
+template <int NW, int LOADS = kStageLoads>
 __device__ __forceinline__ void wait_tile(int ahead, int w) {
-  constexpr int hi = stage_loads_of<NW>(0);
-  constexpr int lo = stage_loads_of<NW>(NW - 1);
-  const bool big = stage_loads_of<NW>(w) == hi;
-  if (ahead >= 2) {
-    if (big) wait_vmcnt<2 * hi>(); else wait_vmcnt<2 * lo>();
-  } else if (ahead == 1) {
-    if (big) wait_vmcnt<hi>(); else wait_vmcnt<lo>();
-  } else {
-    wait_vmcnt<0>();
+  constexpr int hi = stage_loads_of<NW, LOADS>(0);
+  constexpr int lo = stage_loads_of<NW, LOADS>(NW - 1);
+  const bool big = stage_loads_of<NW, LOADS>(w) == hi;
+  switch (ahead) {
+    case 4: if (big) wait_vmcnt<4 * hi>(); else wait_vmcnt<4 * lo>(); break;
+    case 3: if (big) wait_vmcnt<3 * hi>(); else wait_vmcnt<3 * lo>(); break;
+    case 2: if (big) wait_vmcnt<2 * hi>(); else wait_vmcnt<2 * lo>(); break;
+    case 1: if (big) wait_vmcnt<hi>(); else wait_vmcnt<lo>(); break;
+    default: wait_vmcnt<0>(); break;
   }
 }
 
@@ -188,6 +210,56 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ page, int
   }
 }
 
+// INT8 tile staging: loads 0..17 bring the 32 rows' codes (16-byte chunk s
+// of the tile is row s / 36, bytes 16 (s % 36) ..), load 18 brings the 32
+// scales with lanes 0..7.  Rows at or past `rem` re-read row 0's codes; their
+// scales are fetched as they are and never used unmasked.
+template <int NW>
+__device__ __forceinline__ void stage_tile_i8(const uint8_t* __restrict__ page, const float* __restrict__ spage,
+                                              int half, int rem, MLA_LDS uint8_t* stage, int wave, int lane) {
+#pragma unroll
+  for (int i0 = 0; i0 < kI8StageLoads; i0 += NW) {
+    const int i = i0 + wave;
+    if (i < kI8CodeLoads) {
+      const int sl = i * 64 + lane;
+      const int t = sl / 36;
+      const int row = kTileRows * half + t;
+      const int src = (row < rem ? row : 0) * kI8RowBytes + (sl - t * 36) * 16;
+      lds_dma16(page, src, stage + i * 1024);
+    } else if (i == kI8CodeLoads) {
+      if (lane < kTileRows / 4)
+        lds_dma16(reinterpret_cast<const uint8_t*>(spage), (kTileRows * half + 4 * lane) * 4,
+                  stage + kI8CodeBytes);
+    }
+  }
+}
+
+// Two signed int8 codes (bytes 2k, 2k+1 of x) as two exact bf16 values.
+__device__ __forceinline__ unsigned i8pair_to_bf16(unsigned x, int k) {
+  const float f0 = (float)(int)(signed char)(x >> (16 * k));
+  const float f1 = (float)(int)(signed char)(x >> (16 * k + 8));
+  // small integers: the upper 16 bits of the fp32 value are the exact bf16
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+// Convert a staged INT8 tile's codes into exact bf16 values in `cvt`, laid
+// out like a staged bf16 tile (pitch 1184), cooperatively by all threads.
+__device__ __forceinline__ void convert_i8_tile(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt, int tid,
+                                                int nthreads) {
+  for (int c = tid; c < kI8CodeBytes / 16; c += nthreads) {
+    const int t = c / 36, j = c - 36 * t;
+    const u32x4 x = *reinterpret_cast<const MLA_LDS u32x4*>(stage + 16 * c);
+    u32x4 lo, hi;
+    lo[0] = i8pair_to_bf16(x[0], 0); lo[1] = i8pair_to_bf16(x[0], 1);
+    lo[2] = i8pair_to_bf16(x[1], 0); lo[3] = i8pair_to_bf16(x[1], 1);
+    hi[0] = i8pair_to_bf16(x[2], 0); hi[1] = i8pair_to_bf16(x[2], 1);
+    hi[2] = i8pair_to_bf16(x[3], 0); hi[3] = i8pair_to_bf16(x[3], 1);
+    MLA_LDS u32x4* dst = reinterpret_cast<MLA_LDS u32x4*>(cvt + t * kLdsPitch + 32 * j);
+    dst[0] = lo;
+    dst[1] = hi;
+  }
+}
+
 // Per-wave attention state: 16 query rows x 256 value columns.
 struct RowState {
   f32x4 o[kOHalf];   // O^T: lane holds row (lane & 15), columns 256h + 16ct + 4(lane>>4) + e
@@ -244,10 +316,15 @@ constexpr int kVDepth = 3;
 // the tile is visible to this lane's row when tt <= lim (lim >= 31: all).
 // `half` is w / 4; xmine / xpart are this wave's and its partner's 1 KB
 // exchange slots.
+// With SCALED (INT8 cache), `tile` holds the exact integer codes and `tsc`
+// the 32 rows' scales: row t's score is multiplied by tsc[t] and its
+// probability by tsc[t] before the value product (never per element); the
+// row sum uses the unscaled probabilities.
+template <bool SCALED = false>
 __device__ __forceinline__ void attend_tile(const MLA_LDS uint8_t* tile, const bf16x8 (&qf)[kQFrags],
                                             int lim, float scale_log2, int lane, int half,
                                             MLA_LDS f32x4* xmine, const MLA_LDS f32x4* xpart,
-                                            RowState& st) {
+                                            RowState& st, const MLA_LDS float* tsc = nullptr) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
@@ -287,11 +364,20 @@ __device__ __forceinline__ void attend_tile(const MLA_LDS uint8_t* tile, const b
   }
 
   // ---- scale, mask, online softmax (bitwise identical in both waves) ----
+  f32x4 sc_lo = {1.f, 1.f, 1.f, 1.f}, sc_hi = {1.f, 1.f, 1.f, 1.f};
+  if (SCALED) {
+    sc_lo = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 4 * g);
+    sc_hi = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 16 + 4 * g);
+  }
   float s[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     float v0 = lo[e] * scale_log2, v1 = hi[e] * scale_log2;
+    if (SCALED) {
+      v0 *= sc_lo[e];
+      v1 *= sc_hi[e];
+    }
     v0 = 4 * g + e <= lim ? v0 : -INFINITY;
     v1 = 16 + 4 * g + e <= lim ? v1 : -INFINITY;
     s[e] = v0;
@@ -322,8 +408,17 @@ __device__ __forceinline__ void attend_tile(const MLA_LDS uint8_t* tile, const b
   }
   st.l += psum;
   bf16x8 pb;
+  if (SCALED) {
+    // masked rows have probability 0 but possibly a non-finite scale: select, not multiply
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
+    for (int e = 0; e < 4; ++e) {
+      pb[e] = (__bf16)(4 * g + e <= lim ? s[e] * sc_lo[e] : 0.f);
+      pb[4 + e] = (__bf16)(16 + 4 * g + e <= lim ? s[4 + e] * sc_hi[e] : 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- O^T += V^T P^T: 32 rows x this wave's 16 column tiles ----

@@ -76,10 +76,14 @@ __global__ __launch_bounds__(256) void prefill_worklist(PrefillArgs a) {
   }
 }
 
+template <bool I8>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[kStages * kStageBytes];
+  using R = Ring<I8>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[R::stages * R::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[I8 ? kStageBytes : 16];
   __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[kWaves * 64];
   MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
+  MLA_LDS uint8_t* const cvt = (MLA_LDS uint8_t*)cvt_raw;
   MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
   __shared__ int s_pid[kPWin];
   __shared__ int s_tile;
@@ -147,19 +151,32 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent(PrefillArgs
       const int ntiles = min(2 * n, (kv_end - kPage * plo + kTileRows - 1) / kTileRows);
       auto issue = [&](int k) {
         const int p = k >> 1;
-        stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, kv_end - kPage * (plo + p),
-                           ring + (k % kStages) * kStageBytes, w, lane);
+        MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
+        const int rem = kv_end - kPage * (plo + p);
+        if (I8)
+          stage_tile_i8<kWaves>(a.kv + (size_t)s_pid[p] * kI8PageBytes, a.kv_scale + (size_t)s_pid[p] * kPage,
+                                k & 1, rem, stage, w, lane);
+        else
+          stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, rem, stage, w, lane);
       };
-      const int pre = min(kStages - 1, ntiles);
+      const int pre = min(R::stages - 1, ntiles);
       for (int k = 0; k < pre; ++k) issue(k);
       for (int k = 0; k < ntiles; ++k) {
         const int t0 = kPage * plo + kTileRows * k;  // first cache row of tile k
-        wait_tile<kWaves>(min(kStages - 2, ntiles - 1 - k), w);
+        wait_tile<kWaves, R::loads>(min(R::stages - 2, ntiles - 1 - k), w);
         lds_barrier();
-        if (k + kStages - 1 < ntiles) issue(k + kStages - 1);
+        if (k + R::stages - 1 < ntiles) issue(k + R::stages - 1);
+        const MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
+        const MLA_LDS uint8_t* tile = stage;
+        if (I8) {
+          convert_i8_tile(stage, cvt, threadIdx.x, kWaves * 64);
+          lds_write_barrier();
+          tile = cvt;
+        }
         if (wave_rows) {
           const int lim = row_ok ? vis_last - t0 : -1;
-          attend_tile(ring + (k % kStages) * kStageBytes, qf, lim, a.scale_log2, lane, half, xmine, xpart, st);
+          attend_tile<I8>(tile, qf, lim, a.scale_log2, lane, half, xmine, xpart, st,
+                          reinterpret_cast<const MLA_LDS float*>(stage + kI8CodeBytes));
         } else {
           lds_write_barrier();  // the exchange barrier inside attend_tile
         }
@@ -186,11 +203,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent(PrefillArgs
 }
 
 hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream) {
-  (void)kv_dtype;
   hipLaunchKernelGGL(prefill_worklist, dim3(1), dim3(256), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_persistent, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
+  if (kv_dtype == 1)
+    hipLaunchKernelGGL(prefill_persistent<true>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
+  else
+    hipLaunchKernelGGL(prefill_persistent<false>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();
 }
 

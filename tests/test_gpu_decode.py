@@ -216,3 +216,103 @@ def test_decode_workload1_sampled():
     ref_out, ref_lse = oracle.decode(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
     errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, case.name)
     print("workload1 sampled: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)
+
+
+# ---------------------------------------------------------------- INT8 cache
+
+INT8_SMALL = [
+    # (seed, batch, heads, q_len, seq_lens)
+    (501, 1, 16, 1, [256]),
+    (502, 3, 16, 4, [65, 300, 1000]),
+    (503, 4, 32, 2, [33, 64, 127, 2500]),
+    (504, 2, 128, 1, [700, 90]),        # 128 folded rows: two row blocks
+    (505, 1, 16, 4, [4]),
+]
+
+
+@pytest.mark.parametrize("seed,batch,heads,q_len,lens", INT8_SMALL, ids=[str(s[0]) for s in INT8_SMALL])
+def test_decode_int8_matches_oracle(seed, batch, heads, q_len, lens):
+    case = synth.make_decode_case(seed, batch, heads, q_len, seq_lens=lens, kv_dtype="int8")
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, f"int8 seed {seed}")
+
+
+@pytest.mark.parametrize("cus", [1, 7, 256])
+def test_decode_int8_split_plans_agree(cus):
+    case = synth.make_decode_case(506, 3, 16, 2, seq_lens=[1500, 64, 777], kv_dtype="int8")
+    with _cus(cus):
+        out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, f"int8 cus {cus}")
+
+
+def test_decode_int8_nan_scale_poison_has_no_effect():
+    """Tail rows carry code 127 and a NaN scale: the output must not change."""
+    lens = [70, 129, 1]
+    a = synth.make_decode_case(507, 3, 16, 1, seq_lens=lens, max_seq_len=400, kv_dtype="int8")
+    b = synth.make_decode_case(507, 3, 16, 1, seq_lens=lens, max_seq_len=400, kv_dtype="int8",
+                               poison=synth.POISON_NAN)
+    oa, la = run_decode(a)
+    ob, lb = run_decode(b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)) and torch.equal(la, lb)
+    assert torch.isfinite(ob.float()).all()
+
+
+def test_decode_int8_page_permutation_bitwise_invariant():
+    a = synth.make_decode_case(508, 2, 16, 2, seq_lens=[900, 333], kv_dtype="int8")
+    b = synth.make_decode_case(508, 2, 16, 2, seq_lens=[900, 333], kv_dtype="int8")
+    c = b.cache
+    perm = np.random.default_rng(12).permutation(c.num_pages)
+    nd, ns = np.empty_like(c.data), np.empty_like(c.scale)
+    nd[perm] = c.data
+    ns[perm] = c.scale
+    c.data, c.scale = nd, ns
+    c.page_table = perm[c.page_table].astype(np.int32)
+    oa, la = run_decode(a)
+    ob, lb = run_decode(b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)) and torch.equal(la, lb)
+
+
+def test_decode_int8_needle():
+    """A row whose score leads by > 100: the output is that row's dequantised values
+    (the scale enters the value product through the bf16 probability, so the check is
+    the tolerance, not bit equality)."""
+    L = 200
+    case = synth.make_decode_case(509, 2, 16, 1, seq_lens=[L, L], kv_dtype="int8")
+    c = case.cache
+    j = 7
+    for b, pos in enumerate([5, L - 1]):
+        for h in range(16):
+            qq = np.zeros(576, np.uint16)
+            qq[j] = synth.bf16_bits(np.array([64.0], np.float32))[0]
+            case.q[b, h] = qq
+        page, slot = c.page_table[b, pos // 64], pos % 64
+        c.data[page, slot, j] = 127
+        c.scale[page, slot] = np.float32(1.0)
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, "int8 needle")
+
+
+def test_decode_workload4_sampled():
+    """Full-size INT8 decode (8 requests x 4 drafts x 16 heads, 262,144 rows each); the
+    oracle evaluates one draft of two requests, all heads."""
+    case = synth.make_workload(4)
+    out, lse = host(*run_decode(case))
+    toks = [0, 31]
+    ref_out, ref_lse = oracle.decode(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
+    errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, case.name)
+    print("workload4 sampled: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)
+
+
+def test_decode_workload2_sampled():
+    """Ragged 16-request decode (lengths 32K-128K, 32 heads, 2 drafts); sampled rows."""
+    case = synth.make_workload(2)
+    out, lse = host(*run_decode(case))
+    toks = [0, 13, 31]
+    ref_out, ref_lse = oracle.decode(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
+    errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, case.name)
+    print("workload2 sampled: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)

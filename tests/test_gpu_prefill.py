@@ -87,3 +87,14 @@ def test_prefill_workload3_sampled():
     ref_out, ref_lse = oracle.prefill(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
     errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, case.name)
     print("workload3 sampled: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)
+
+
+@pytest.mark.parametrize("seed,heads,prefix,new", [(420, 16, [100, 0, 64], [5, 70, 1]),
+                                                   (421, 128, [77, 10], [3, 2]),
+                                                   (422, 16, [1000, 63], [17, 9])])
+def test_prefill_int8_matches_oracle(seed, heads, prefix, new):
+    case = synth.make_prefill_case(seed, heads, prefix_lens=prefix, new_lens=new, kv_dtype="int8")
+    out, lse = host(*run_prefill(case))
+    ref_out, ref_lse = oracle.prefill(case)
+    T = case.total_q()
+    assert_close(out[:T], lse[:T], ref_out, ref_lse, f"int8 seed {seed}")
