@@ -80,6 +80,78 @@ __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& 
   }
 }
 
+// Wave 0 of workgroup g locates its share floor(g*P/G) .. floor((g+1)*P/G)
+// of the page stream and the (request, page) where it starts; workgroup
+// (0, 0) also records the page prefix sums for the merge.
+__device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lane, int* s_info) {
+  const int G = a.grid;
+  long long P = 0;
+  const bool write_cum = g == 0 && blockIdx.y == 0 && G > 1;
+  for (int base = 0; base < a.batch; base += 64) {
+    const int b = base + lane;
+    const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
+    const int incl = wave_incl_scan(np, lane);
+    if (write_cum && b < a.batch) a.cum_pages[b] = (int)(P + incl - np);
+    P += __shfl(incl, 63);
+  }
+  if (write_cum && lane == 0) a.cum_pages[a.batch] = (int)P;
+  const long long lo = P * g / G, hi = P * (g + 1) / G;
+  int b0 = a.batch, j0 = 0;
+  if (lo < hi) {
+    long long run = 0;
+    for (int base = 0; base < a.batch; base += 64) {
+      const int b = base + lane;
+      const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
+      const int incl = wave_incl_scan(np, lane);
+      const long long before = run + incl - np;
+      const bool hit = np > 0 && before <= lo && lo < before + np;
+      const unsigned long long mask = __ballot(hit);
+      if (mask) {
+        const int src = __ffsll((long long)mask) - 1;
+        b0 = base + src;
+        j0 = (int)(lo - (run + __shfl(incl - np, src)));
+        break;
+      }
+      run += __shfl(incl, 63);
+    }
+  }
+  if (lane == 0) {
+    s_info[0] = (int)lo;
+    s_info[1] = (int)hi;
+    s_info[2] = b0;
+    s_info[3] = j0;
+  }
+}
+
+// Fill the window's page list: pages wlo .. wlo + n - 1 of the stream,
+// starting at request cb, page cj; returns the cursor after them.
+__device__ __forceinline__ void fill_window(const DecodeArgs& a, int n, int& cb, int& cj, int* s_pid, int* s_req,
+                                            int* s_rem, int nthreads) {
+  for (int k = threadIdx.x; k < n; k += nthreads) {
+    int b = cb, off = cj + k, Lc;
+    for (;;) {
+      Lc = clamp_len(a.seq_lens[b], a.max_pages);
+      const int np = (Lc + kPage - 1) / kPage;
+      if (off < np || b + 1 >= a.batch) break;
+      off -= np;
+      ++b;
+    }
+    off = min(off, a.max_pages - 1);  // never past the table, whatever the lengths say
+    s_pid[k] = a.page_table[(size_t)b * a.max_pages + off];
+    s_req[k] = b;
+    s_rem[k] = Lc - kPage * off;
+  }
+  int b = cb, off = cj + n;  // advance the cursor by n pages (uniform across the workgroup)
+  for (;;) {
+    const int np = (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage;
+    if (off < np || b + 1 >= a.batch) break;
+    off -= np;
+    ++b;
+  }
+  cb = b;
+  cj = off;
+}
+
 // Phase one.  blockIdx.x: share of the page stream; blockIdx.y: block of 64
 // folded rows (requests with more than 64 rows use two).  I8: INT8 cache,
 // staged as codes + row scales and converted to exact bf16 per tile.
@@ -100,45 +172,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
   const int G = a.grid;
   const int g = blockIdx.x;
 
-  // ---- locate this workgroup's share of the page stream (wave 0) ----
-  if (w == 0) {
-    long long P = 0;
-    const bool write_cum = g == 0 && blockIdx.y == 0 && G > 1;
-    for (int base = 0; base < a.batch; base += 64) {
-      const int b = base + lane;
-      const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
-      const int incl = wave_incl_scan(np, lane);
-      if (write_cum && b < a.batch) a.cum_pages[b] = (int)(P + incl - np);
-      P += __shfl(incl, 63);
-    }
-    if (write_cum && lane == 0) a.cum_pages[a.batch] = (int)P;
-    const long long lo = P * g / G, hi = P * (g + 1) / G;
-    int b0 = a.batch, j0 = 0;
-    if (lo < hi) {
-      long long run = 0;
-      for (int base = 0; base < a.batch; base += 64) {
-        const int b = base + lane;
-        const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
-        const int incl = wave_incl_scan(np, lane);
-        const long long before = run + incl - np;
-        const bool hit = np > 0 && before <= lo && lo < before + np;
-        const unsigned long long mask = __ballot(hit);
-        if (mask) {
-          const int src = __ffsll((long long)mask) - 1;
-          b0 = base + src;
-          j0 = (int)(lo - (run + __shfl(incl - np, src)));
-          break;
-        }
-        run += __shfl(incl, 63);
-      }
-    }
-    if (lane == 0) {
-      s_info[0] = (int)lo;
-      s_info[1] = (int)hi;
-      s_info[2] = b0;
-      s_info[3] = j0;
-    }
-  }
+  if (w == 0) locate_share(a, g, lane, s_info);
   __syncthreads();
   const int seg_lo = s_info[0], seg_hi = s_info[1];
   if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
@@ -161,31 +195,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
   for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
     const int n = min(kWin, seg_hi - wlo);
     __syncthreads();  // the previous window's list and stages are no longer read
-    for (int k = threadIdx.x; k < n; k += kWaves * 64) {
-      int b = cb, off = cj + k, Lc;
-      for (;;) {
-        Lc = clamp_len(a.seq_lens[b], a.max_pages);
-        const int np = (Lc + kPage - 1) / kPage;
-        if (off < np || b + 1 >= a.batch) break;
-        off -= np;
-        ++b;
-      }
-      off = min(off, a.max_pages - 1);  // never past the table, whatever the lengths say
-      s_pid[k] = a.page_table[(size_t)b * a.max_pages + off];
-      s_req[k] = b;
-      s_rem[k] = Lc - kPage * off;
-    }
-    {  // advance the window cursor by n pages (uniform across the workgroup)
-      int b = cb, off = cj + n;
-      for (;;) {
-        const int np = (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage;
-        if (off < np || b + 1 >= a.batch) break;
-        off -= np;
-        ++b;
-      }
-      cb = b;
-      cj = off;
-    }
+    fill_window(a, n, cb, cj, s_pid, s_req, s_rem, kWaves * 64);
     __syncthreads();
 
     // Tiles are half pages: tile k is half (k & 1) of window page k >> 1.
@@ -234,6 +244,164 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
     }
   }
   if (wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
+}
+
+
+// Fill the window's tile list: the valid tiles (half pages holding at least
+// one of their request's rows) of pages wlo .. wlo + n - 1 of the stream,
+// starting at request cb, page cj, in stream order.  Tile t: page s_pid[t],
+// request s_req[t] >> 1, half s_req[t] & 1, s_rem[t] = the request's rows
+// from the tile's first row (> 0).  Wave 0 builds the list; every thread
+// advances the cursor past the n pages.  Returns the tile count through
+// s_info[0].
+__device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, int n, int& cb, int& cj, int* s_pid,
+                                                  int* s_req, int* s_rem, int* s_count, int w, int lane) {
+  if (w == 0) {
+    int base = 0;
+    for (int k0 = 0; k0 < n; k0 += 64) {
+      const int k = k0 + lane;
+      int nt = 0, b = cb, off = cj + k, Lc = 0;
+      if (k < n) {
+        for (;;) {
+          Lc = clamp_len(a.seq_lens[b], a.max_pages);
+          const int np = (Lc + kPage - 1) / kPage;
+          if (off < np || b + 1 >= a.batch) break;
+          off -= np;
+          ++b;
+        }
+        off = min(off, a.max_pages - 1);  // never past the table, whatever the lengths say
+        nt = Lc - kPage * off > kTileRows ? 2 : 1;
+      }
+      const int incl = wave_incl_scan(nt, lane);
+      if (k < n) {
+        const int t = base + incl - nt;
+        const int pid = a.page_table[(size_t)b * a.max_pages + off];
+        const int rem = Lc - kPage * off;
+        s_pid[t] = pid;
+        s_req[t] = 2 * b;
+        s_rem[t] = rem;
+        if (nt == 2) {
+          s_pid[t + 1] = pid;
+          s_req[t + 1] = 2 * b + 1;
+          s_rem[t + 1] = rem - kTileRows;
+        }
+      }
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) *s_count = base;
+  }
+  int b = cb, off = cj + n;  // advance the cursor by n pages (uniform across the workgroup)
+  for (;;) {
+    const int np = (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage;
+    if (off < np || b + 1 >= a.batch) break;
+    off -= np;
+    ++b;
+  }
+  cb = b;
+  cj = off;
+}
+
+// Phase one for a bf16 cache, software-pipelined across tiles.  The
+// window's tiles are processed in segments of one request each.  Step t of
+// a segment waits for tile t (the only load in flight), passes one
+// workgroup barrier, starts tile t + 1 into the third ring stage, and then
+// computes the scores of tile t interleaved with the softmax of tile t - 1,
+// hands its half of the scores to the partner wave through a
+// double-buffered exchange, and accumulates the values of tile t - 1.  The
+// first step of a segment only computes scores; after its last step one
+// more barrier lets the partners finish the segment's last tile.  Query
+// fragments are loaded and partials written only between segments.
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[kPStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[2 * kWaves * 64];
+  MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
+  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
+  __shared__ int s_pid[2 * kWin], s_req[2 * kWin], s_rem[2 * kWin];
+  __shared__ int s_info[5];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = blockIdx.x;
+  if (w == 0) locate_share(a, g, lane, s_info);
+  __syncthreads();
+  const int seg_lo = s_info[0], seg_hi = s_info[1];
+  if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
+  int cb = s_info[2], cj = s_info[3];
+
+  const int half = w >> 2;
+  const int row = kBlockRows * blockIdx.y + 16 * (w & 3) + (lane & 15);
+  const bool wave_rows = kBlockRows * blockIdx.y + 16 * (w & 3) < a.rows;
+  const bool row_ok = row < a.rows;
+  const int draft = row_ok ? row / a.heads : 0;
+  const int late = a.q_len - draft;  // row sees rows t <= L - late
+  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
+  MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
+  auto stage = [&](int t) { return ring + (t % kPStages) * kStageBytes; };
+
+  RowState st;
+  bf16x8 qf[kQFrags];
+  int cur_b = -1;
+
+  for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
+    const int n = min(kWin, seg_hi - wlo);
+    __syncthreads();  // the previous window's list and stages are no longer read
+    fill_window_tiles(a, n, cb, cj, s_pid, s_req, s_rem, &s_info[4], w, lane);
+    __syncthreads();
+    const int N = s_info[4];
+    auto issue = [&](int t) {
+      stage_tile<kWaves>(a.kv + (size_t)s_pid[t] * kPageBytes, s_req[t] & 1, s_rem[t] + kTileRows * (s_req[t] & 1),
+                         stage(t), w, lane);
+    };
+    issue(0);
+    for (int t0 = 0; t0 < N;) {
+      const int b = s_req[t0] >> 1;
+      int t1 = t0 + 1;
+      while (t1 < N && (s_req[t1] >> 1) == b) ++t1;
+      if (wave_rows && b != cur_b) {
+        if (cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
+        load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+        reset_state(st);
+      }
+      cur_b = b;
+      // first step: scores only
+      wait_vmcnt<0>();
+      lds_write_barrier();
+      if (t0 + 1 < N) issue(t0 + 1);
+      f32x4 s_prev = {0.f, 0.f, 0.f, 0.f};
+      if (wave_rows) {
+        s_prev = tile_scores(stage(t0), qf, lane, half);
+        xmine[(t0 & 1) * kWaves * 64] = s_prev;
+      }
+      int prev_lim = s_rem[t0] - late;
+      for (int t = t0 + 1; t < t1; ++t) {
+        wait_vmcnt<0>();
+        lds_write_barrier();
+        if (t + 1 < N) issue(t + 1);
+        const int lim = s_rem[t] - late;
+        if (wave_rows) {
+          const f32x4 other = xpart[((t - 1) & 1) * kWaves * 64];
+          const f32x4 lo = half == 0 ? s_prev : other;
+          const f32x4 hi = half == 0 ? other : s_prev;
+          s_prev = tile_step(stage(t), stage(t - 1), qf, lo, hi, prev_lim, a.scale_log2, lane, half, st);
+          xmine[(t & 1) * kWaves * 64] = s_prev;
+        }
+        prev_lim = lim;
+      }
+      // last tile of the segment
+      lds_write_barrier();
+      if (wave_rows) {
+        const f32x4 other = xpart[((t1 - 1) & 1) * kWaves * 64];
+        const f32x4 lo = half == 0 ? s_prev : other;
+        const f32x4 hi = half == 0 ? other : s_prev;
+        float alpha;
+        const bf16x8 pb = tile_softmax(lo, hi, prev_lim, a.scale_log2, lane, st, alpha);
+        rescale_o(st, alpha);
+        tile_values(stage(t1 - 1), pb, lane, half, st);
+      }
+      t0 = t1;
+    }
+  }
+  if (wave_rows && cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
 }
 
 // Phase two: per (request, row), reduce the partials of the workgroups
@@ -301,7 +469,7 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_
   if (kv_dtype == 1)
     hipLaunchKernelGGL(decode_phase1<true>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   else
-    hipLaunchKernelGGL(decode_phase1<false>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL(decode_phase1_pipe, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.grid == 1) return e;
   const int total_rows = args.batch * args.rows;

@@ -437,6 +437,133 @@ __device__ __forceinline__ void attend_tile(const MLA_LDS uint8_t* tile, const b
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined core (bf16 cache).  A wave's work on a tile is split into three
+// parts so that consecutive tiles overlap: while the score MFMAs of tile k
+// run, the same wave's VALU performs the softmax of tile k-1, and the value
+// product of tile k-1 follows.  Two tiles are resident (k-1 for values, k for
+// scores) and one is loading, so the ring has three stages; one 37 KB tile
+// in flight per CU already saturates HBM on gfx950 (measured: ~5.7 TB/s).
+// ---------------------------------------------------------------------------
+constexpr int kPStages = 3;
+
+// Scores of this wave's 16 rows of the tile against its 16 query rows: the
+// 18 k-steps alternate between two accumulators (two independent MFMA
+// chains), summed at the end.
+__device__ __forceinline__ f32x4 tile_scores(const MLA_LDS uint8_t* tile, const bf16x8 (&qf)[kQFrags],
+                                             int lane, int half) {
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const MLA_LDS uint8_t* kbase = tile + tile_off(16 * half + r16, g);
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 kb[kKDepth + 1];
+#pragma unroll
+  for (int d = 0; d < kKDepth; ++d) kb[d] = lds_b128(kbase + 64 * d);
+#pragma unroll
+  for (int ks = 0; ks < kQFrags; ++ks) {
+    if (ks + kKDepth < kQFrags) kb[(ks + kKDepth) % (kKDepth + 1)] = lds_b128(kbase + 64 * (ks + kKDepth));
+    if (ks & 1)
+      a1 = mfma16x16x32(kb[ks % (kKDepth + 1)], qf[ks], a1);
+    else
+      a0 = mfma16x16x32(kb[ks % (kKDepth + 1)], qf[ks], a0);
+  }
+  return a0 + a1;
+}
+
+// Online softmax of one tile from the two score halves (lo: tile rows
+// 4g + e, hi: 16 + 4g + e), bitwise identical in both partner waves.  The
+// running max and sum are updated here; the factor alpha by which the value
+// accumulators must be rescaled is returned and applied by the caller
+// (rescale_o), only when some row's max was raised, so that this code stays
+// one branch-free block that can be interleaved with the next tile's score
+// MFMAs.  Returns the probabilities in the B-operand layout of the value
+// product.
+__device__ __forceinline__ bf16x8 tile_softmax(f32x4 lo, f32x4 hi, int lim, float scale_log2, int lane,
+                                               RowState& st, float& alpha) {
+  const int g = lane >> 4;
+  float s[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v0 = lo[e] * scale_log2, v1 = hi[e] * scale_log2;
+    v0 = 4 * g + e <= lim ? v0 : -INFINITY;
+    v1 = 16 + 4 * g + e <= lim ? v1 : -INFINITY;
+    s[e] = v0;
+    s[4 + e] = v1;
+    mx = fmaxf(mx, fmaxf(v0, v1));
+  }
+  mx = wave_max_rows(mx);
+  const float m_new = mx > st.m + kRescaleSlack ? mx : st.m;
+  // unchanged max: exactly 1 (also when both are -inf); first finite max: 0
+  alpha = m_new == st.m ? 1.f : fast_exp2(st.m - m_new);
+  st.m = m_new;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s[i] = fast_exp2(s[i] - m_use);
+    psum += s[i];
+  }
+  st.l = st.l * alpha + psum;
+  bf16x8 pb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
+  return pb;
+}
+
+// Apply a raised max to the value accumulators; skipped (uniform branch)
+// when no row of the wave changed its max, the common case after the first
+// tiles of a range.
+__device__ __forceinline__ void rescale_o(RowState& st, float alpha) {
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int ct = 0; ct < kOHalf; ++ct) st.o[ct] *= alpha;
+  }
+}
+
+// Value product of one tile for this wave's 256 value columns.
+__device__ __forceinline__ void tile_values(const MLA_LDS uint8_t* tile, bf16x8 pb, int lane, int half,
+                                            RowState& st) {
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+  const int colq = 4 * (i16 & 3);
+  const int tq = 4 * g + (i16 >> 2);
+  const MLA_LDS uint8_t* vbase = tile + tq * kLdsPitch + colq * 2 + 512 * half;
+  bf16x4 vb[kVDepth + 1][2];
+#pragma unroll
+  for (int d = 0; d < kVDepth; ++d) {
+    vb[d][0] = lds_tr16(vbase + 32 * d);
+    vb[d][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * d);
+  }
+#pragma unroll
+  for (int ct = 0; ct < kOHalf; ++ct) {
+    if (ct + kVDepth < kOHalf) {
+      vb[(ct + kVDepth) % (kVDepth + 1)][0] = lds_tr16(vbase + 32 * (ct + kVDepth));
+      vb[(ct + kVDepth) % (kVDepth + 1)][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * (ct + kVDepth));
+    }
+    const bf16x4 v0 = vb[ct % (kVDepth + 1)][0], v1 = vb[ct % (kVDepth + 1)][1];
+    bf16x8 va;
+    va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
+    va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
+    st.o[ct] = mfma16x16x32(va, pb, st.o[ct]);
+  }
+}
+
+// Steady-state step of the pipeline: scores of tile k (returned) with the
+// softmax of tile k-1 interleaved into the MFMA chain, then the value
+// product of tile k-1.  Scores and softmax are independent and in one
+// basic block, so the VALU work can issue while the MFMAs execute.
+__device__ __forceinline__ f32x4 tile_step(const MLA_LDS uint8_t* tile_k, const MLA_LDS uint8_t* tile_prev,
+                                           const bf16x8 (&qf)[kQFrags], f32x4 lo, f32x4 hi, int lim,
+                                           float scale_log2, int lane, int half, RowState& st) {
+  const f32x4 sc = tile_scores(tile_k, qf, lane, half);
+  float alpha;
+  const bf16x8 pb = tile_softmax(lo, hi, lim, scale_log2, lane, st, alpha);
+  rescale_o(st, alpha);
+  tile_values(tile_prev, pb, lane, half, st);
+  return sc;
+}
+
 // Row totals at the end of a range: the row's full sum, 1/sum (0 when the
 // row saw nothing), and the log-sum-exp in log2 units (-inf when empty).
 __device__ __forceinline__ void finish_row(const RowState& st, float& inv, float& lse2) {
