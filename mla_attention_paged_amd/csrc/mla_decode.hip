@@ -80,28 +80,45 @@ __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& 
   }
 }
 
+// Clamped request lengths, cached in LDS for the first kLenCache requests
+// (the tile-list walks read them repeatedly; the cache keeps those reads
+// off the global-memory latency chain in front of the first tile).
+constexpr int kLenCache = 512;
+
+struct Lens {
+  const DecodeArgs& a;
+  const int* cache;
+  __device__ int operator()(int b) const {
+    return b < kLenCache ? cache[b] : clamp_len(a.seq_lens[b], a.max_pages);
+  }
+};
+
 // Wave 0 of workgroup g locates its share floor(g*P/G) .. floor((g+1)*P/G)
-// of the page stream and the (request, page) where it starts; workgroup
-// (0, 0) also records the page prefix sums for the merge.
-__device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lane, int* s_info) {
+// of the page stream and the (request, page) where it starts, and fills the
+// length cache; workgroup (0, 0) also records the page prefix sums for the
+// merge.
+__device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lane, int* s_info, int* s_len) {
   const int G = a.grid;
   long long P = 0;
   const bool write_cum = g == 0 && blockIdx.y == 0 && G > 1;
   for (int base = 0; base < a.batch; base += 64) {
     const int b = base + lane;
-    const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
+    const int L = b < a.batch ? clamp_len(a.seq_lens[b], a.max_pages) : 0;
+    if (b < a.batch && b < kLenCache) s_len[b] = L;
+    const int np = (L + kPage - 1) / kPage;
     const int incl = wave_incl_scan(np, lane);
     if (write_cum && b < a.batch) a.cum_pages[b] = (int)(P + incl - np);
     P += __shfl(incl, 63);
   }
   if (write_cum && lane == 0) a.cum_pages[a.batch] = (int)P;
+  const Lens lens{a, s_len};  // this wave's own LDS writes are visible to its later reads
   const long long lo = P * g / G, hi = P * (g + 1) / G;
   int b0 = a.batch, j0 = 0;
   if (lo < hi) {
     long long run = 0;
     for (int base = 0; base < a.batch; base += 64) {
       const int b = base + lane;
-      const int np = b < a.batch ? (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage : 0;
+      const int np = b < a.batch ? (lens(b) + kPage - 1) / kPage : 0;
       const int incl = wave_incl_scan(np, lane);
       const long long before = run + incl - np;
       const bool hit = np > 0 && before <= lo && lo < before + np;
@@ -125,12 +142,12 @@ __device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lan
 
 // Fill the window's page list: pages wlo .. wlo + n - 1 of the stream,
 // starting at request cb, page cj; returns the cursor after them.
-__device__ __forceinline__ void fill_window(const DecodeArgs& a, int n, int& cb, int& cj, int* s_pid, int* s_req,
-                                            int* s_rem, int nthreads) {
+__device__ __forceinline__ void fill_window(const DecodeArgs& a, const Lens& lens, int n, int& cb, int& cj,
+                                            int* s_pid, int* s_req, int* s_rem, int nthreads) {
   for (int k = threadIdx.x; k < n; k += nthreads) {
     int b = cb, off = cj + k, Lc;
     for (;;) {
-      Lc = clamp_len(a.seq_lens[b], a.max_pages);
+      Lc = lens(b);
       const int np = (Lc + kPage - 1) / kPage;
       if (off < np || b + 1 >= a.batch) break;
       off -= np;
@@ -143,7 +160,7 @@ __device__ __forceinline__ void fill_window(const DecodeArgs& a, int n, int& cb,
   }
   int b = cb, off = cj + n;  // advance the cursor by n pages (uniform across the workgroup)
   for (;;) {
-    const int np = (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage;
+    const int np = (lens(b) + kPage - 1) / kPage;
     if (off < np || b + 1 >= a.batch) break;
     off -= np;
     ++b;
@@ -166,14 +183,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
   MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
   __shared__ int s_pid[kWin], s_req[kWin], s_rem[kWin];
   __shared__ int s_info[4];
+  __shared__ int s_len[kLenCache];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int G = a.grid;
   const int g = blockIdx.x;
 
-  if (w == 0) locate_share(a, g, lane, s_info);
+  if (w == 0) locate_share(a, g, lane, s_info, s_len);
   __syncthreads();
+  const Lens lens{a, s_len};
   const int seg_lo = s_info[0], seg_hi = s_info[1];
   if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
   int cb = s_info[2], cj = s_info[3];
@@ -191,11 +210,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
   RowState st;
   bf16x8 qf[kQFrags];
   int cur_b = -1;
+  // The first request's query loads start now, overlapping the tile-list
+  // fill and the first tile; the first tile's wait covers them.
+  int q_b = -1;  // request whose query fragments are loaded or in flight
+  if (wave_rows && cb < a.batch) {
+    issue_q(row_ok ? a.q + ((size_t)cb * a.rows + row) * kDqk : nullptr, lane, qf);
+    q_b = cb;
+  }
 
   for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
     const int n = min(kWin, seg_hi - wlo);
     __syncthreads();  // the previous window's list and stages are no longer read
-    fill_window(a, n, cb, cj, s_pid, s_req, s_rem, kWaves * 64);
+    fill_window(a, lens, n, cb, cj, s_pid, s_req, s_rem, kWaves * 64);
     __syncthreads();
 
     // Tiles are half pages: tile k is half (k & 1) of window page k >> 1.
@@ -220,7 +246,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
         if (cur_b >= 0 && wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
         cur_b = b;
         if (wave_rows) {
-          load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+          if (b != q_b) load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+          q_b = -1;
           reset_state(st);
         }
       }
@@ -254,8 +281,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
 // from the tile's first row (> 0).  Wave 0 builds the list; every thread
 // advances the cursor past the n pages.  Returns the tile count through
 // s_info[0].
-__device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, int n, int& cb, int& cj, int* s_pid,
-                                                  int* s_req, int* s_rem, int* s_count, int w, int lane) {
+__device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, const Lens& lens, int n, int& cb, int& cj,
+                                                  int* s_pid, int* s_req, int* s_rem, int* s_count, int w, int lane) {
   if (w == 0) {
     int base = 0;
     for (int k0 = 0; k0 < n; k0 += 64) {
@@ -263,7 +290,7 @@ __device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, int n, in
       int nt = 0, b = cb, off = cj + k, Lc = 0;
       if (k < n) {
         for (;;) {
-          Lc = clamp_len(a.seq_lens[b], a.max_pages);
+          Lc = lens(b);
           const int np = (Lc + kPage - 1) / kPage;
           if (off < np || b + 1 >= a.batch) break;
           off -= np;
@@ -292,7 +319,7 @@ __device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, int n, in
   }
   int b = cb, off = cj + n;  // advance the cursor by n pages (uniform across the workgroup)
   for (;;) {
-    const int np = (clamp_len(a.seq_lens[b], a.max_pages) + kPage - 1) / kPage;
+    const int np = (lens(b) + kPage - 1) / kPage;
     if (off < np || b + 1 >= a.batch) break;
     off -= np;
     ++b;
@@ -318,12 +345,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
   __shared__ int s_pid[2 * kWin], s_req[2 * kWin], s_rem[2 * kWin];
   __shared__ int s_info[5];
+  __shared__ int s_len[kLenCache];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = blockIdx.x;
-  if (w == 0) locate_share(a, g, lane, s_info);
+  if (w == 0) locate_share(a, g, lane, s_info, s_len);
   __syncthreads();
+  const Lens lens{a, s_len};
   const int seg_lo = s_info[0], seg_hi = s_info[1];
   if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
   int cb = s_info[2], cj = s_info[3];
@@ -341,11 +370,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   RowState st;
   bf16x8 qf[kQFrags];
   int cur_b = -1;
+  // The first request's query loads start now, overlapping the tile-list
+  // fill and the first tile; the first tile's wait covers them.
+  int q_b = -1;  // request whose query fragments are loaded or in flight
+  if (wave_rows && cb < a.batch) {
+    issue_q(row_ok ? a.q + ((size_t)cb * a.rows + row) * kDqk : nullptr, lane, qf);
+    q_b = cb;
+  }
 
   for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
     const int n = min(kWin, seg_hi - wlo);
     __syncthreads();  // the previous window's list and stages are no longer read
-    fill_window_tiles(a, n, cb, cj, s_pid, s_req, s_rem, &s_info[4], w, lane);
+    fill_window_tiles(a, lens, n, cb, cj, s_pid, s_req, s_rem, &s_info[4], w, lane);
     __syncthreads();
     const int N = s_info[4];
     auto issue = [&](int t) {
@@ -359,7 +395,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
       while (t1 < N && (s_req[t1] >> 1) == b) ++t1;
       if (wave_rows && b != cur_b) {
         if (cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
-        load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+        if (b != q_b) load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+        q_b = -1;
         reset_state(st);
       }
       cur_b = b;
@@ -405,32 +442,44 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
 }
 
 // Phase two: per (request, row), reduce the partials of the workgroups
-// whose shares intersect the request.  One workgroup per (row, half of the
-// value columns): a first pass takes the max partial log2-sum-exp, then wave
-// w accumulates shares w, w+4, ... (lane: 4 consecutive columns) and the
-// four waves are combined through LDS.
+// whose shares intersect the request: lse = log2-sum-exp of the partial
+// lses, out = sum_s 2^(lse_s - lse) o_s.  One workgroup per (row, quarter of
+// the value columns).  The share weights 2^(lse_s - m) are computed once
+// into LDS (m: the max partial lse; empty shares weigh 0); then thread
+// (group j, quad c) accumulates shares j, j + 8, ... for columns 4c .. 4c+3
+// of the quarter, with all its loads of a batch of shares in flight at once,
+// and the eight groups are combined through LDS.  Empty shares read the
+// first share's (written, finite) slot with weight 0, so bytes of the
+// workspace that phase one did not write never enter the sums.
+constexpr int kMergeGroups = 8;
+constexpr int kMergeChunk = 256;  // share weights held in LDS at a time
+
 __device__ __forceinline__ bool share_empty(long long P, int G, int gg) {
   return P * gg / G >= P * (gg + 1) / G;
 }
 
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  __shared__ float s_wgt[kMergeChunk];
   __shared__ float s_red[4];
-  __shared__ float s_w[4];
-  __shared__ f32x4 s_acc[4][64];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  __shared__ f32x4 s_acc[kMergeGroups][32];
+  __shared__ float s_ws[kMergeGroups];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int R = blockIdx.x;
-  const int half = blockIdx.y;
+  const int quarter = blockIdx.y;
   const int b = R / a.rows, row = R - b * a.rows;
   const long long P = a.cum_pages[a.batch];
   const int G = a.grid;
   const long long p0 = a.cum_pages[b], p1 = a.cum_pages[b + 1];
   if (p1 <= p0) return;
   const int g0 = owner_group(p0, P, G), g1 = owner_group(p1 - 1, P, G);
+  const int ns = g1 - g0 + 1;
+  const float* lse_col = a.part_lse + (size_t)(g0 + b) * a.rows + row;  // share i: lse_col[i * rows]
 
   float m = -INFINITY;
-  for (int gg = g0 + (int)threadIdx.x; gg <= g1; gg += 256)
-    if (!share_empty(P, G, gg)) m = fmaxf(m, a.part_lse[(size_t)(gg + b) * a.rows + row]);
+  for (int i = tid; i < ns; i += 256)
+    if (!share_empty(P, G, g0 + i)) m = fmaxf(m, lse_col[(size_t)i * a.rows]);
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
   if (lane == 0) s_red[w] = m;
@@ -438,29 +487,54 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float m_use = m == -INFINITY ? 0.f : m;
 
-  float wsum = 0.f;
+  const int grp = tid >> 5, quad = tid & 31;
+  const int col = quarter * (kDv / 4) + 4 * quad;
+  const float* o_col = a.part_o + ((size_t)(g0 + b) * a.rows + row) * kDv + col;  // share i: + i * rows * 512
+  const size_t share_stride = (size_t)a.rows * kDv;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int col = half * (kDv / 2) + 4 * lane;
-#pragma unroll 4
-  for (int gg = g0 + w; gg <= g1; gg += 4) {
-    if (share_empty(P, G, gg)) continue;
-    const size_t slot = (size_t)(gg + b) * a.rows + row;
-    const float wgt = fast_exp2(a.part_lse[slot] - m_use);
-    wsum += wgt;
-    acc += *reinterpret_cast<const f32x4*>(a.part_o + slot * kDv + col) * wgt;
+  float wsum = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += kMergeChunk) {
+    const int nc = min(kMergeChunk, ns - c0);
+    __syncthreads();  // the previous chunk's weights are no longer read
+    if (tid < nc) {
+      const int i = c0 + tid;
+      s_wgt[tid] = share_empty(P, G, g0 + i) ? 0.f : fast_exp2(lse_col[(size_t)i * a.rows] - m_use);
+    }
+    __syncthreads();
+    for (int k0 = grp; k0 < nc; k0 += 8 * kMergeGroups) {
+      f32x4 v[8];
+      float wt[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u * kMergeGroups;
+        wt[u] = k < nc ? s_wgt[k] : 0.f;
+        const int i = wt[u] > 0.f ? c0 + k : 0;  // zero weight: the first share's slot
+        v[u] = *reinterpret_cast<const f32x4*>(o_col + (size_t)i * share_stride);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc += v[u] * wt[u];
+        wsum += wt[u];
+      }
+    }
   }
-  s_acc[w][lane] = acc;
-  if (lane == 0) s_w[w] = wsum;
+  s_acc[grp][quad] = acc;
+  if (quad == 0) s_ws[grp] = wsum;
   __syncthreads();
-  if (w == 0) {
-    const float tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
-    const f32x4 o = s_acc[0][lane] + s_acc[1][lane] + s_acc[2][lane] + s_acc[3][lane];
+  if (tid < 32) {
+    f32x4 o = s_acc[0][tid];
+    float tot = s_ws[0];
+#pragma unroll
+    for (int j = 1; j < kMergeGroups; ++j) {
+      o += s_acc[j][tid];
+      tot += s_ws[j];
+    }
     const float inv = tot > 0.f ? 1.0f / tot : 0.f;
     bf16x4 h;
     h[0] = (__bf16)(o[0] * inv); h[1] = (__bf16)(o[1] * inv);
     h[2] = (__bf16)(o[2] * inv); h[3] = (__bf16)(o[3] * inv);
     *reinterpret_cast<bf16x4*>(a.out + (size_t)R * kDv + col) = h;
-    if (half == 0 && lane == 0) a.lse[R] = tot > 0.f ? (m_use + fast_log2(tot)) * kLn2 : -INFINITY;
+    if (quarter == 0 && tid == 0) a.lse[R] = tot > 0.f ? (m_use + fast_log2(tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -473,7 +547,7 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.grid == 1) return e;
   const int total_rows = args.batch * args.rows;
-  hipLaunchKernelGGL(decode_merge, dim3(total_rows, 2), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL(decode_merge, dim3(total_rows, 4), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -274,6 +274,14 @@ __device__ __forceinline__ void reset_state(RowState& st) {
   st.l = 0.f;
 }
 
+// Start loading this wave's Q fragments (no wait; see load_q).
+__device__ __forceinline__ void issue_q(const uint16_t* __restrict__ qrow, int lane, bf16x8 (&qf)[kQFrags]) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < kQFrags; ++ks)
+    qf[ks] = qrow ? *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g) : bf16x8{};
+}
+
 // Load this wave's Q fragments: lane holds row (lane & 15), features
 // 32*ks + 8*(lane>>4) .. +7 for each k-step ks.  `qrow` is null for rows
 // past the end of the block (they attend with a zero query and are never
