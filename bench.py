@@ -26,7 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
        python bench.py --record-traffic FETCH_DIR WRITE_DIR [--calib-copy-mb M]
 
 The roofline's ``traffic`` is the HBM bytes per decode call read from
-profiles/decode_traffic.json (written by --record-traffic from two
+profiles/mla_decode_b4_h16_q4_L64K_traffic.json (written by --record-traffic from two
 rocprofv3 counter runs); it is null when the kernel sources have changed
 since those counters were taken.
 """
@@ -109,7 +109,7 @@ def time_calls(fn_list, stream, warmup: int, steps: int) -> float:
 KERNEL_SOURCES = ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_decode.hip",
                   "mla_attention_paged_amd/csrc/mla_prefill.hip", "mla_attention_paged_amd/csrc/mla_device.h",
                   "mla_attention_paged_amd/csrc/mla_internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_decode_b4_h16_q4_L64K_traffic.json")
 
 
 def sources_digest() -> str:
@@ -155,7 +155,7 @@ def _counter_means(path: str):
 
 def record_traffic(fetch_dir: str, write_dir: str, calib_mb: int) -> int:
     """Turn the FETCH_SIZE and WRITE_SIZE runs of this script (with --calib-copy-mb) into
-    profiles/decode_traffic.json: HBM bytes per decode call, each counter scaled by the
+    profiles/mla_decode_b4_h16_q4_L64K_traffic.json: HBM bytes per decode call, each counter scaled by the
     factor that maps its reading of the calibration copy onto the copy's true size."""
     calib = calib_mb * (1 << 20)
     fetch, fcopy = _counter_means(fetch_dir)
@@ -202,7 +202,7 @@ def main() -> int:
                     help="also run a plain device-to-device copy of this many MiB (3 times), whose "
                          "HBM counter readings calibrate the per-kernel FETCH_SIZE / WRITE_SIZE figures")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU work: write profiles/decode_traffic.json from the two rocprofv3 counter runs")
+                    help="no GPU work: write profiles/mla_decode_b4_h16_q4_L64K_traffic.json from the two rocprofv3 counter runs")
     args = ap.parse_args()
     if args.record_traffic:
         return record_traffic(args.record_traffic[0], args.record_traffic[1], args.calib_copy_mb or 1024)
