@@ -40,7 +40,7 @@ DecodePlan plan_decode(int batch, int heads, int q_len, int max_seq_len, int kv_
     const size_t slots = (size_t)(p.grid + batch) * rows;
     size_t off = 0;
     p.part_o_off = off;
-    off = align256(off + slots * kDv * sizeof(float));
+    off = align256(off + slots * kDv * sizeof(uint16_t));  // bf16 partial outputs
     p.part_lse_off = off;
     off = align256(off + slots * sizeof(float));
     p.cum_off = off;
@@ -235,7 +235,7 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
   a.lse = lse;
   if (plan.grid > 1) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    a.part_o = reinterpret_cast<float*>(ws + plan.part_o_off);
+    a.part_o = reinterpret_cast<uint16_t*>(ws + plan.part_o_off);
     a.part_lse = reinterpret_cast<float*>(ws + plan.part_lse_off);
     a.cum_pages = reinterpret_cast<int32_t*>(ws + plan.cum_off);
   }

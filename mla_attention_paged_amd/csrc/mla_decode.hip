@@ -55,6 +55,9 @@ __device__ __forceinline__ int owner_group(long long p, long long P, int G) {
 // Write the rows of one finished (request, share) pair: the final output
 // when phase one is the only phase, else the partial in slot `slot`.  Wave
 // half h writes value columns 256h .. 256h + 255; half 0 writes the LSE.
+// Partial outputs are normalised (o / sum, a weighted mean of value rows)
+// and stored in bf16 like the final output, halving the workspace traffic;
+// their log2-sum-exp stays fp32.
 __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& st, int b, int slot,
                                            int row, bool row_ok, int half, int lane) {
   float inv, lse2;
@@ -62,21 +65,21 @@ __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& 
   if (!row_ok) return;
   const int g = lane >> 4;
   const int col0 = (kDv / 2) * half + 4 * g;
-  if (a.grid == 1) {
-    uint16_t* dst = a.out + ((size_t)b * a.rows + row) * kDv + col0;
+  const bool final_out = a.grid == 1;
+  uint16_t* dst = (final_out ? a.out + ((size_t)b * a.rows + row) * kDv
+                             : a.part_o + ((size_t)slot * a.rows + row) * kDv) + col0;
 #pragma unroll
-    for (int ct = 0; ct < kOHalf; ++ct) {
-      const f32x4 v = st.o[ct] * inv;
-      bf16x4 h;
-      h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
-      *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
-    }
-    if (g == 0 && half == 0) a.lse[(size_t)b * a.rows + row] = lse2 * kLn2;
-  } else {
-    float* dst = a.part_o + ((size_t)slot * a.rows + row) * kDv + col0;
-#pragma unroll
-    for (int ct = 0; ct < kOHalf; ++ct) *reinterpret_cast<f32x4*>(dst + 16 * ct) = st.o[ct] * inv;
-    if (g == 0 && half == 0) a.part_lse[(size_t)slot * a.rows + row] = lse2;
+  for (int ct = 0; ct < kOHalf; ++ct) {
+    const f32x4 v = st.o[ct] * inv;
+    bf16x4 h;
+    h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+    *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
+  }
+  if (g == 0 && half == 0) {
+    if (final_out)
+      a.lse[(size_t)b * a.rows + row] = lse2 * kLn2;
+    else
+      a.part_lse[(size_t)slot * a.rows + row] = lse2;
   }
 }
 
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 
   const int grp = tid >> 5, quad = tid & 31;
   const int col = quarter * (kDv / 4) + 4 * quad;
-  const float* o_col = a.part_o + ((size_t)(g0 + b) * a.rows + row) * kDv + col;  // share i: + i * rows * 512
+  const uint16_t* o_col = a.part_o + ((size_t)(g0 + b) * a.rows + row) * kDv + col;  // share i: + i * rows * 512
   const size_t share_stride = (size_t)a.rows * kDv;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
@@ -509,7 +512,8 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
         const int k = k0 + u * kMergeGroups;
         wt[u] = k < nc ? s_wgt[k] : 0.f;
         const int i = wt[u] > 0.f ? c0 + k : 0;  // zero weight: the first share's slot
-        v[u] = *reinterpret_cast<const f32x4*>(o_col + (size_t)i * share_stride);
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(o_col + (size_t)i * share_stride);
+        v[u] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {

@@ -29,7 +29,7 @@ struct DecodeArgs {
   float scale_log2;           // softmax_scale * log2(e)
   uint16_t* out;              // bf16 [batch * rows, 512]
   float* lse;                 // fp32 [batch * rows]
-  float* part_o;              // workspace: [(grid + batch) * rows, 512]
+  uint16_t* part_o;           // workspace: bf16 [(grid + batch) * rows, 512], normalised partial outputs
   float* part_lse;            // workspace: [(grid + batch) * rows], log2 units
   int32_t* cum_pages;         // workspace: [batch + 1] page prefix sums
 };
