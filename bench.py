@@ -16,6 +16,10 @@ The prefill leg times ``mla_prefill_varlen`` on
 ``prefill_b8_h16_P16K-96K_N200-2000`` and reports TFLOP/s of the absorbed
 form as called (2 * 1088 flops per visible (query row, cached row) pair).
 
+The append leg times ``mla_kv_append`` writing that prefill workload's 8,629
+new rows into a bf16 and an INT8 cache (bytes: rows read plus rows and scales
+written); at ~20 MB per call it is partly launch-bound.
+
 The CPU baseline is the fp64 oracle on the host's cores (at most 16
 threads), timed on the full decode workload (all 16 query tokens, all
 heads), repeated until about 10 s of CPU work have run; it is a reported
@@ -177,9 +181,9 @@ def record_traffic(fetch_dir: str, write_dir: str, calib_mb: int) -> int:
            "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
            "calibration": f"plain device copy of {calib_mb} MiB (torch copy_), largest copy dispatch reading",
            "commands": [f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -f csv -d {fetch_dir} -o fetch -- "
-                        f"python3 bench.py --steps 5 --no-prefill --no-cpu-baseline --calib-copy-mb {calib_mb}",
+                        f"python3 bench.py --steps 5 --no-prefill --no-append --no-cpu-baseline --calib-copy-mb {calib_mb}",
                         f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -f csv -d {write_dir} -o write -- "
-                        f"python3 bench.py --steps 5 --no-prefill --no-cpu-baseline --calib-copy-mb {calib_mb}",
+                        f"python3 bench.py --steps 5 --no-prefill --no-append --no-cpu-baseline --calib-copy-mb {calib_mb}",
                         f"python3 bench.py --record-traffic {fetch_dir} {write_dir} --calib-copy-mb {calib_mb}"]}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
@@ -197,6 +201,7 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), whose "
@@ -309,6 +314,41 @@ def main() -> int:
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
         }
+
+    # ---------------- append leg: the prefill workload's new rows into the cache ----------------
+    if not args.no_append:
+        acase = synth.make_workload(3)
+        pt = acase.cache.page_table
+        num_pages = int(pt.max()) + 1
+        rows = int(acase.cu_seqlens_q[-1])
+        g = torch.Generator(device="cuda").manual_seed(7)
+        new = torch.randn((rows, 576), generator=g, device="cuda").to(torch.bfloat16)
+        cu = torch.from_numpy(acase.cu_seqlens_q.astype(np.int32)).cuda()
+        start = torch.from_numpy(acase.prefix_lens.astype(np.int32)).cuda()
+        pt_d = torch.from_numpy(np.ascontiguousarray(pt, dtype=np.int32)).cuda()
+        legs = {}
+        for kind, name in ((mla.MLA_KV_BF16, "bf16"), (mla.MLA_KV_INT8, "int8")):
+            if kind == mla.MLA_KV_BF16:
+                kv = torch.zeros((num_pages, 64, 576), dtype=torch.bfloat16, device="cuda")
+                sc = None
+                row_out = 1152
+            else:
+                kv = torch.zeros((num_pages, 64, 576), dtype=torch.int8, device="cuda")
+                sc = torch.ones((num_pages, 64), dtype=torch.float32, device="cuda")
+                row_out = 576 + 4
+
+            def acall(kv=kv, sc=sc, kind=kind):
+                mla.mla_kv_append(new, cu, start, kv, sc, kind, pt_d, pt.shape[1], acase.batch, rows, 64, stream)
+
+            asteps = 200
+            ams = time_calls([acall], stream, 20, asteps) / asteps
+            abytes = rows * (1152 + row_out)  # rows read + rows (and scales) written
+            legs[name] = {"us_per_call": round(ams * 1e3, 2), "GBps": round(abytes / (ams * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(abytes / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "bytes_per_call": abytes}
+            del kv, sc
+        result["append"] = {"workload": f"{acase.name} new rows ({rows} rows of 576, at their prefix positions)",
+                            "kernel": "mla_kv_append", "bound": "hbm", **legs}
 
     # ---------------- counter calibration: a plain copy of known size ----------------
     if args.calib_copy_mb > 0:

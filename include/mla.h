@@ -177,6 +177,46 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
                        float softmax_scale, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* hip_stream);
 
+/*
+ * mla_kv_append -- write the rows of new tokens into their requests' pages.
+ *
+ * The step that precedes attention: decode and prefill read a request's new
+ * tokens from the cache [TALK, section "Kernel：让 MLA 真正跑满 GPU": the
+ * attention kernels run over the paged latent cache, and at long prefixes
+ * decode stays bandwidth-bound even with an INT8 latent cache].  For request
+ * b, new row j (0 <= j < n_b = cu_seqlens_new[b+1] - cu_seqlens_new[b]) is
+ * row cu_seqlens_new[b] + j of kv_new and goes to logical position
+ * t = start_pos[b] + j of the request: page page_table[b][t / 64], slot t % 64.
+ *
+ *   bf16 cache (kv_dtype 0): the 576 values are copied unchanged.
+ *   int8 cache (kv_dtype 1): symmetric per-row quantisation with an fp32
+ *     scale: scale = max_c |x_c| / 127 (fp32 division, rounded to nearest;
+ *     an all-zero row gets scale 1), code_c = clamp(rint(x_c / scale),
+ *     -127, 127) with ties to even; the codes go to the row of the int8 cache
+ *     and the scale to kv_scale[page * 64 + slot].  Dequantised value:
+ *     code * scale, as the attention entry points read it.
+ *
+ *   kv_new          bf16 [total_new, 576] (latent | rope)
+ *   cu_seqlens_new  int32 [batch+1], cu_seqlens_new[0] = 0, nondecreasing,
+ *                   cu_seqlens_new[batch] = total_new
+ *   start_pos       int32 [batch]: logical position of each request's first
+ *                   new row (its cached length before the append)
+ *   kv_cache        bf16 or int8 [num_pages, 64, 576], written in place
+ *   kv_scale        fp32 [num_pages, 64] for an int8 cache (written), else NULL
+ *   page_table      int32 [batch, max_pages_per_req]
+ *
+ * Rows whose position falls outside 0 .. max_pages_per_req * 64 - 1 are not
+ * written.  Nothing else of the cache is touched.  The page-table entries of
+ * the written positions must name existing pages (a precondition, as for the
+ * attention entry points).  Returns MLA_ERR_UNSUPPORTED for page_size != 64
+ * or an unknown kv_dtype, MLA_ERR_INVALID for null pointers (when
+ * total_new > 0), batch < 1, total_new < 0, max_pages_per_req < 1 or an
+ * int8 cache without kv_scale.  total_new == 0 enqueues nothing.
+ */
+int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32_t* start_pos,
+                  void* kv_cache, float* kv_scale, int kv_dtype, const int32_t* page_table,
+                  int max_pages_per_req, int batch, int total_new, int page_size, void* hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(int status);
 

@@ -54,6 +54,8 @@ def library():
         lib.mla_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
                                            f32, vp, vp, vp, sz, vp]
         lib.mla_prefill_varlen.restype = i32
+        lib.mla_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp]
+        lib.mla_kv_append.restype = i32
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(sz)]
@@ -123,3 +125,11 @@ def mla_prefill_varlen(q, cu_seqlens_q, prefix_lens, kv_cache, kv_scale, kv_dtyp
                                       float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                       int(workspace_bytes), _stream(hip_stream))
     _check(rc, "mla_prefill_varlen")
+
+
+def mla_kv_append(kv_new, cu_seqlens_new, start_pos, kv_cache, kv_scale, kv_dtype, page_table,
+                  max_pages_per_req, batch, total_new, page_size, hip_stream=None) -> None:
+    rc = library().mla_kv_append(_ptr(kv_new), _ptr(cu_seqlens_new), _ptr(start_pos), _ptr(kv_cache),
+                                 _ptr(kv_scale), kv_dtype, _ptr(page_table), max_pages_per_req, batch,
+                                 total_new, page_size, _stream(hip_stream))
+    _check(rc, "mla_kv_append")

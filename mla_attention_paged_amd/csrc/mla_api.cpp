@@ -295,4 +295,31 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32_t* start_pos,
+                  void* kv_cache, float* kv_scale, int kv_dtype, const int32_t* page_table,
+                  int max_pages_per_req, int batch, int total_new, int page_size, void* hip_stream) {
+  if (batch < 1 || total_new < 0 || max_pages_per_req < 1) return MLA_ERR_INVALID;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (total_new > 0 && (!kv_new || !cu_seqlens_new || !start_pos || !kv_cache || !page_table))
+    return MLA_ERR_INVALID;
+  if (kv_dtype == MLA_KV_INT8 && !kv_scale) return MLA_ERR_INVALID;
+  if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if ((long long)max_pages_per_req * MLA_PAGE_SIZE > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (total_new == 0) return MLA_OK;
+
+  AppendArgs a{};
+  a.kv_new = static_cast<const uint16_t*>(kv_new);
+  a.cu = cu_seqlens_new;
+  a.start_pos = start_pos;
+  a.kv = static_cast<uint8_t*>(kv_cache);
+  a.kv_scale = kv_dtype == MLA_KV_INT8 ? kv_scale : nullptr;  // the kernel keys on it
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_req;
+  a.batch = batch;
+  a.total_new = total_new;
+  const hipError_t e = launch_append(a, kv_dtype, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 }  // extern "C"

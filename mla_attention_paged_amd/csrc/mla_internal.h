@@ -56,6 +56,18 @@ struct PrefillArgs {
   int32_t* counter;           // workspace: work-queue head
 };
 
+struct AppendArgs {
+  const uint16_t* kv_new;     // bf16 [total_new, 576]
+  const int32_t* cu;          // [batch + 1] new-row offsets
+  const int32_t* start_pos;   // [batch] logical position of each request's first new row
+  uint8_t* kv;                // pages, bf16 or int8 rows, written in place
+  float* kv_scale;            // int8 only: [num_pages, 64]
+  const int32_t* page_table;  // [batch, max_pages]
+  int max_pages;
+  int batch;
+  int total_new;
+};
+
 struct DecodePlan {
   int grid;                   // phase-one workgroups (1: single pass, no merge)
   int waves;                  // waves per workgroup (4 or 8)
@@ -77,5 +89,6 @@ PrefillPlan plan_prefill(int batch, int heads, int max_q_len, int total_q, int m
 
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& args, int kv_dtype, hipStream_t stream);
 
 }  // namespace mla

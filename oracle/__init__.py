@@ -5,7 +5,8 @@ leg may import this package.  The library's compute path never does.
 
 ``mla_oracle.c`` holds the definition (see its header for the passages it
 follows); this module compiles it with gcc when the shared object is missing
-or older than the source, and wraps it with ctypes.
+or older than the source, and wraps it with ctypes.  ``kv_append.py`` is the
+oracle of the step that writes new tokens' rows into the pages.
 """
 from __future__ import annotations
 
@@ -137,3 +138,6 @@ def prefill(case, tokens=None, bounds=None, nthreads=None):
     c = case.cache
     return attention(case.q, c.data, c.scale, c.page_table, case.cu_seqlens_q, c.kv_lens,
                      case.softmax_scale, tokens=tokens, bounds=bounds, nthreads=nthreads)
+
+
+from .kv_append import kv_append, quantize_row  # noqa: E402  (oracle of the append step)

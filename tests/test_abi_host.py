@@ -123,3 +123,29 @@ def test_workspace_size_argument_checks(lib):
     assert lib.mla_splitkv_workspace_size(0, 16, 4, 16, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
     assert lib.mla_splitkv_workspace_size(4, 16, 4, 3, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
     assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 7, ctypes.byref(out)) == mla.MLA_ERR_UNSUPPORTED
+
+
+def _append_rc(lib, **kw):
+    a = dict(new=1, cu=1, start=1, kv=1, scale=None, kind=0, pt=1, maxp=16, batch=2, total=8, page=64,
+             stream=None)
+    a.update(kw)
+    return lib.mla_kv_append(a["new"], a["cu"], a["start"], a["kv"], a["scale"], a["kind"], a["pt"],
+                             a["maxp"], a["batch"], a["total"], a["page"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(new=None), mla.MLA_ERR_INVALID),
+    (dict(cu=None), mla.MLA_ERR_INVALID),
+    (dict(start=None), mla.MLA_ERR_INVALID),
+    (dict(kv=None), mla.MLA_ERR_INVALID),
+    (dict(pt=None), mla.MLA_ERR_INVALID),
+    (dict(batch=0), mla.MLA_ERR_INVALID),
+    (dict(total=-1), mla.MLA_ERR_INVALID),
+    (dict(maxp=0), mla.MLA_ERR_INVALID),
+    (dict(kind=1), mla.MLA_ERR_INVALID),            # int8 without scales
+    (dict(kind=2), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(total=0, new=None, kv=None), mla.MLA_OK),  # nothing to write, nothing enqueued
+])
+def test_append_argument_checks(lib, kw, code):
+    assert _append_rc(lib, **kw) == code
