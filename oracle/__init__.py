@@ -48,6 +48,8 @@ def load_library(path: str):
     lib.mla_oracle_attention_split.argtypes = common + [_i32p, ctypes.c_int, _i32p, ctypes.c_int,
                                                         _dblp, _dblp, ctypes.c_int]
     lib.mla_oracle_attention_split.restype = ctypes.c_int
+    lib.mla_oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.mla_oracle_e4m3_value.restype = ctypes.c_double
     return lib
 
 
@@ -77,19 +79,19 @@ def attention(q_bits: np.ndarray, cache: np.ndarray, kv_scale: Optional[np.ndarr
               nthreads: Optional[int] = None, lib=None):
     """Attention for the given query tokens (all tokens when ``tokens`` is None).
 
-    q_bits: uint16 bf16 bits [total_q, H, dqk]; cache: uint16 bf16 bits or int8
-    [num_pages, page_size, dqk]; kv_scale: float32 [num_pages, page_size] for
-    int8; page_table int32 [batch, max_pages]; q_start int32 [batch+1];
+    q_bits: uint16 bf16 bits [total_q, H, dqk]; cache: uint16 bf16 bits, int8
+    codes or uint8 E4M3 codes [num_pages, page_size, dqk]; kv_scale: float32
+    [num_pages, page_size] for int8 and fp8; page_table int32 [batch, max_pages]; q_start int32 [batch+1];
     kv_len int32 [batch].  ``bounds`` selects the split form.  Returns
     (out float64 [n, H, dv], lse float64 [n, H]).
     """
     lib = lib or _load()
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
-    if cache.dtype == np.int8:
-        kind = 1
+    if cache.dtype in (np.int8, np.uint8):
+        kind = 1 if cache.dtype == np.int8 else 2
         cache = np.ascontiguousarray(cache)
         if kv_scale is None:
-            raise ValueError("int8 cache needs kv_scale")
+            raise ValueError("int8 / fp8 cache needs kv_scale")
         kv_scale = np.ascontiguousarray(kv_scale, dtype=np.float32)
     else:
         kind = 0
@@ -140,4 +142,9 @@ def prefill(case, tokens=None, bounds=None, nthreads=None):
                      case.softmax_scale, tokens=tokens, bounds=bounds, nthreads=nthreads)
 
 
-from .kv_append import kv_append, quantize_row  # noqa: E402  (oracle of the append step)
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 code byte, as the attention oracle decodes it."""
+    return float(_load().mla_oracle_e4m3_value(int(code) & 0xFF))
+
+
+from .kv_append import kv_append, quantize_row, quantize_row_fp8, e4m3_round  # noqa: E402

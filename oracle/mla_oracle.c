@@ -15,6 +15,8 @@
  *          article, sections "TokenSpeed 技術簡介" and "TokenSpeed 性能預覽".
  *   [MLA]  The published MLA formulation (DeepSeek-V2, arXiv:2405.04434),
  *          used only for the absorbed form and the 192-wide score scale.
+ *   [GITREAD] "TokenSpeed 深度解析:把 LLM 推理压到"光速"意味着什么" --
+ *          third-party project commentary, section "核心技术揭秘".
  *
  * What is computed (the plain definition; every kernel technique on the
  * pages -- folding the query axis into the heads, split-KV, paging, online
@@ -39,7 +41,17 @@
  *     out_d = sum_t exp(s_t - lse) * c_t[d],  d < dv
  *
  *   Row gather: c_t = cache[page_table[b][t / page_size]][t % page_size];
- *   for the INT8 cache c_t[d] = code * scale[page][slot].
+ *   for the INT8 cache c_t[d] = code * scale[page][slot]; for the FP8 cache
+ *   c_t[d] = e4m3(code) * scale[page][slot].
+ *
+ *   FP8 [GITREAD] "TokenSpeed 深度解析:把 LLM 推理压到"光速"意味着什么",
+ *   section "核心技术揭秘": FP8 KV-cache quantisation is named as standard,
+ *   with no format given.  Read here as the 8-bit "E4M3" format of the OCP
+ *   8-bit floating point specification (finite variant): sign bit 7,
+ *   exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 encodes
+ *   the subnormals m * 2^-9; the all-ones magnitude 0x7F is NaN; there is no
+ *   infinity, so the largest finite magnitude is 448.  Each row carries an
+ *   fp32 scale as the INT8 cache does.
  *
  *   Split form [TALK, "Kernel：让 MLA 真正跑满 GPU": phase one computes
  *   split-KV partial results, phase two reduces them]: for a partition of
@@ -48,7 +60,7 @@
  *   lse = ln sum_k exp(lse_k) and out = sum_k exp(lse_k - lse) * o_k.
  *
  * Inputs are read exactly as the GPU receives them (bf16 bit patterns, int8
- * codes with fp32 scales) and widened exactly to double.
+ * or fp8 codes with fp32 scales) and widened exactly to double.
  */
 #include <math.h>
 #include <pthread.h>
@@ -60,7 +72,7 @@ enum { ORACLE_OK = 0, ORACLE_EINVAL = 1 };
 
 typedef struct {
     const uint16_t *q;
-    int kv_kind; /* 0: bf16 rows, 1: int8 codes + fp32 per-row scale */
+    int kv_kind; /* 0: bf16 rows, 1: int8 codes, 2: fp8 e4m3 codes; 1, 2: + fp32 per-row scale */
     const void *cache;
     const float *kv_scale;
     int num_pages;
@@ -89,6 +101,19 @@ static double bf16_to_double(uint16_t h)
     return (double)f;
 }
 
+/* Value of an E4M3 code, from the format's definition (see the header). */
+double mla_oracle_e4m3_value(uint8_t code)
+{
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
 /* Request that owns global query token tok: q_start[b] <= tok < q_start[b+1]. */
 static int owner_of(const job_t *j, int tok)
 {
@@ -108,10 +133,14 @@ static int gather_row(const job_t *j, int b, int t, double *c)
     if (j->kv_kind == 0) {
         const uint16_t *row = (const uint16_t *)j->cache + base;
         for (int d = 0; d < j->dqk; ++d) c[d] = bf16_to_double(row[d]);
-    } else {
+    } else if (j->kv_kind == 1) {
         const int8_t *row = (const int8_t *)j->cache + base;
         double s = (double)j->kv_scale[(size_t)page * j->page_size + slot];
         for (int d = 0; d < j->dqk; ++d) c[d] = (double)row[d] * s;
+    } else {
+        const uint8_t *row = (const uint8_t *)j->cache + base;
+        double s = (double)j->kv_scale[(size_t)page * j->page_size + slot];
+        for (int d = 0; d < j->dqk; ++d) c[d] = mla_oracle_e4m3_value(row[d]) * s;
     }
     return ORACLE_OK;
 }
@@ -247,8 +276,8 @@ static int check_common(const job_t *j)
 {
     if (!j->q || !j->cache || !j->page_table || !j->q_start || !j->kv_len || !j->out || !j->lse)
         return ORACLE_EINVAL;
-    if (j->kv_kind == 1 && !j->kv_scale) return ORACLE_EINVAL;
-    if (j->kv_kind != 0 && j->kv_kind != 1) return ORACLE_EINVAL;
+    if (j->kv_kind != 0 && !j->kv_scale) return ORACLE_EINVAL;
+    if (j->kv_kind < 0 || j->kv_kind > 2) return ORACLE_EINVAL;
     if (j->batch < 1 || j->H < 1 || j->dqk < 1 || j->dv < 1 || j->dv > j->dqk || j->page_size < 1)
         return ORACLE_EINVAL;
     if (j->ntokens < 0) return ORACLE_EINVAL;

@@ -19,6 +19,12 @@ Recipe (all deterministic from one integer seed):
   3. bf16 values are round-to-nearest-even of the float32 draws.
   4. INT8: per 576-wide row, scale = max|x| / 127 in fp32, code =
      clip(rint(x / scale), -127, 127).
+  4b. FP8 (E4M3 codes, uint8): per row, the codes are |x| * 64 truncated
+     onto the E4M3 grid (3 mantissa bits; magnitudes below 2^-6 become 0,
+     above 448 become 448; the sign of x in bit 7), and the fp32 scale is
+     2^-6 * (1 + |x_0| / 16) with x_0 the row's first draw.  This is a
+     generator recipe only: it is not the rounding of the append step, and
+     the codes and scales are simply the inputs.
   5. Slots past a request's length in its last page, and the poison page that
      every unused page-table entry points at, hold a poison value (bf16
      1000.0 by default, optionally NaN).
@@ -76,6 +82,23 @@ def quantize_int8_rows(x: np.ndarray):
     return codes, scale
 
 
+def fp8_codes_from_draws(x: np.ndarray):
+    """Recipe 4b: E4M3 code bytes and per-row scales from float32 draws [..., 576]."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64) * 64.0
+    _, ex = np.frexp(a)
+    E = ex - 1                                   # a in [2^E, 2^(E+1))
+    m = np.floor((a / np.ldexp(1.0, E) - 1.0) * 8.0).astype(np.int64)
+    e = E.astype(np.int64) + 7
+    big = (e > 15) | ((e == 15) & (m == 7))
+    e = np.where(big, 15, e)
+    m = np.where(big, 6, m)
+    mag = np.where(e >= 1, (e << 3) | m, 0)
+    codes = (mag | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+    scale = (np.float32(2.0 ** -6) * (np.float32(1.0) + np.abs(x[..., 0]) / np.float32(16.0))).astype(np.float32)
+    return codes, scale
+
+
 def _normal_chunks(seed: int, stream: int, shape_rows: int, row_shape: tuple, chunk: int,
                    sink) -> None:
     """Fill rows [0, shape_rows) chunk by chunk; ``sink(r0, r1, values_f32)`` stores each chunk."""
@@ -98,9 +121,9 @@ def _normal_chunks(seed: int, stream: int, shape_rows: int, row_shape: tuple, ch
 @dataclass
 class PagedCache:
     """A paged latent cache as the kernels see it."""
-    kv_dtype: str                 # "bf16" or "int8"
-    data: np.ndarray              # uint16 bf16 bits or int8, [num_pages, page_size, 576]
-    scale: Optional[np.ndarray]   # float32 [num_pages, page_size] for int8, else None
+    kv_dtype: str                 # "bf16", "int8" or "fp8"
+    data: np.ndarray              # uint16 bf16 bits, int8 or uint8 E4M3 codes, [num_pages, page_size, 576]
+    scale: Optional[np.ndarray]   # float32 [num_pages, page_size] for int8 and fp8, else None
     page_table: np.ndarray        # int32 [batch, max_pages]
     kv_lens: np.ndarray           # int32 [batch]: cached rows per request, new tokens included
     poison_page: int
@@ -146,8 +169,8 @@ def build_paged_cache(rng: np.random.Generator, seed: int, kv_lens, kv_dtype: st
     if kv_dtype == "bf16":
         data = np.empty((pool, page_size, D_QK), dtype=np.uint16)
         scale = None
-    elif kv_dtype == "int8":
-        data = np.empty((pool, page_size, D_QK), dtype=np.int8)
+    elif kv_dtype in ("int8", "fp8"):
+        data = np.empty((pool, page_size, D_QK), dtype=np.int8 if kv_dtype == "int8" else np.uint8)
         scale = np.empty((pool, page_size), dtype=np.float32)
     else:
         raise ValueError(f"unknown kv dtype {kv_dtype!r}")
@@ -157,7 +180,7 @@ def build_paged_cache(rng: np.random.Generator, seed: int, kv_lens, kv_dtype: st
         if kv_dtype == "bf16":
             data[phys] = bf16_bits(x)
         else:
-            codes, s = quantize_int8_rows(x)
+            codes, s = quantize_int8_rows(x) if kv_dtype == "int8" else fp8_codes_from_draws(x)
             data[phys] = codes
             scale[phys] = s
 
@@ -168,7 +191,8 @@ def build_paged_cache(rng: np.random.Generator, seed: int, kv_lens, kv_dtype: st
         pbits = bf16_bits(np.array([poison], dtype=np.float32))[0]
         data[poison_page] = pbits
     else:
-        data[poison_page] = 127
+        pcode = 127 if kv_dtype == "int8" else 0x7E   # the largest code: 127, or E4M3 448
+        data[poison_page] = pcode
         scale[poison_page] = np.float32(poison)
     for b in range(batch):
         L = int(kv_lens[b])
@@ -179,7 +203,7 @@ def build_paged_cache(rng: np.random.Generator, seed: int, kv_lens, kv_dtype: st
             if kv_dtype == "bf16":
                 data[pg, used:] = pbits
             else:
-                data[pg, used:] = 127
+                data[pg, used:] = pcode
                 scale[pg, used:] = np.float32(poison)
     return PagedCache(kv_dtype, data, scale, page_table, kv_lens, poison_page, page_size)
 
