@@ -202,6 +202,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-scaled", action="store_true",
+                    help="skip the INT8 / FP8 cache decode leg on the 64K decode shape")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), whose "
@@ -315,6 +317,37 @@ def main() -> int:
                          "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
         }
 
+    # ---------------- scaled caches: the 64K decode shape with INT8 and FP8 rows ----------------
+    if not args.no_scaled:
+        legs = {}
+        for dt in ("int8", "fp8"):
+            scase = synth.make_decode_case(2, case.batch, case.heads, case.q_len,  # workload 1 seed
+                                           seq_lens=case.seq_lens.tolist(), kv_dtype=dt)
+            sin = decode_inputs(scase)
+            skv = [sin["kv"]] + [sin["kv"].clone() for _ in range(max(0, args.copies - 1))]
+            sws_b = mla.mla_splitkv_workspace_size(scase.batch, H, scase.q_len, T, scase.max_seq_len, sin["kind"])
+            sws = torch.empty(max(sws_b, 1), dtype=torch.uint8, device="cuda")
+
+            def make_scall(kv, sin=sin, scase=scase, sws=sws):
+                def call():
+                    mla.mla_decode(sin["q"], kv, sin["scale"], sin["kind"], sin["pt"], scase.cache.max_pages,
+                                   sin["seq_lens"], scase.batch, scase.q_len, H, 64, scase.max_seq_len,
+                                   scase.softmax_scale, out, lse, sws, sws.numel(), stream)
+                return call
+
+            ssteps = max(20, args.steps // 2)
+            sms = time_calls([make_scall(kv) for kv in skv], stream, max(10, args.warmup // 2), ssteps) / ssteps
+            sbytes = decode_algorithmic_bytes(scase)
+            gbs = sbytes / (sms * 1e-3) / 1e9
+            legs[dt] = {"us_per_call": round(sms * 1e3, 2), "GBps": round(gbs, 1),
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": sbytes,
+                        "tflops": round(decode_flops(scase) / (sms * 1e-3) / 1e12, 1)}
+            del skv, sin, sws
+            torch.cuda.empty_cache()
+        result["scaled_cache_decode"] = {"workload": f"{case.name} with INT8 / FP8 (E4M3) rows and fp32 row scales",
+                                         "kernel": "mla_decode call (decode_phase1<scaled> + decode_merge)",
+                                         "bound": "hbm", **legs}
+
     # ---------------- append leg: the prefill workload's new rows into the cache ----------------
     if not args.no_append:
         acase = synth.make_workload(3)
@@ -327,13 +360,14 @@ def main() -> int:
         start = torch.from_numpy(acase.prefix_lens.astype(np.int32)).cuda()
         pt_d = torch.from_numpy(np.ascontiguousarray(pt, dtype=np.int32)).cuda()
         legs = {}
-        for kind, name in ((mla.MLA_KV_BF16, "bf16"), (mla.MLA_KV_INT8, "int8")):
+        for kind, name in ((mla.MLA_KV_BF16, "bf16"), (mla.MLA_KV_INT8, "int8"), (mla.MLA_KV_FP8, "fp8")):
             if kind == mla.MLA_KV_BF16:
                 kv = torch.zeros((num_pages, 64, 576), dtype=torch.bfloat16, device="cuda")
                 sc = None
                 row_out = 1152
             else:
-                kv = torch.zeros((num_pages, 64, 576), dtype=torch.int8, device="cuda")
+                kv = torch.zeros((num_pages, 64, 576), dtype=torch.int8 if name == "int8" else torch.uint8,
+                                 device="cuda")
                 sc = torch.ones((num_pages, 64), dtype=torch.float32, device="cuda")
                 row_out = 576 + 4
 

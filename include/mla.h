@@ -7,6 +7,8 @@
  *          talk transcript.
  *   [NEWS] "英偉達力薦，小團隊兩個月開源一款「光速級」智能體推理引擎" -- news
  *          article on the TokenSpeed blog post.
+ *   [GITREAD] "TokenSpeed 深度解析:把 LLM 推理压到"光速"意味着什么" --
+ *          third-party commentary on the project.
  *
  * What is computed.  [TALK, section "Kernel：让 MLA 真正跑满 GPU"]: MLA keeps
  * the KV of every head as one compressed latent row per token, and the first
@@ -29,9 +31,19 @@
  *
  * Memory layouts (all device memory, all row-major, no padding):
  *   query      bf16 [tokens, num_heads, 576]
- *   kv_cache   bf16 or int8 [num_pages, page_size, 576]; page_size must be 64
- *   kv_scale   fp32 [num_pages, page_size]: per-row scale of the int8 cache
- *              (row value = code * scale); NULL for a bf16 cache
+ *   kv_cache   bf16, int8 or fp8 [num_pages, page_size, 576]; page_size must
+ *              be 64
+ *   kv_scale   fp32 [num_pages, page_size]: per-row scale of the int8 and
+ *              fp8 caches (row value = code * scale, or e4m3(code) * scale);
+ *              NULL for a bf16 cache
+ *
+ * FP8 cache [GITREAD] "TokenSpeed 深度解析:把 LLM 推理压到"光速"意味着什么",
+ * section "核心技术揭秘" (FP8 KV-cache quantisation, no format given): codes
+ * are OCP E4M3, finite variant -- sign bit 7, exponent bits 6..3 with bias
+ * 7, mantissa bits 2..0, subnormals m * 2^-9, largest magnitude 448; the
+ * magnitude 0x7F (NaN) must not occur in a cache.  Codes are widened to
+ * bf16 exactly; attention then runs as for bf16 with the row scales applied
+ * to the scores and probabilities.
  *   page_table int32 [batch, max_pages_per_req]: physical page of logical
  *              page j of request b; only entries j < ceil(L_b / 64) are read
  *   out        bf16 [tokens, num_heads, 512]
@@ -77,6 +89,7 @@ extern "C" {
 /* Cache element types. */
 #define MLA_KV_BF16 0
 #define MLA_KV_INT8 1
+#define MLA_KV_FP8 2  /* E4M3 codes, see the layouts above */
 
 #define MLA_DIM_QK 576      /* cache row / query row width: 512 latent + 64 rope */
 #define MLA_DIM_V 512       /* value width: the first 512 columns of a row */
@@ -195,14 +208,20 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
  *     -127, 127) with ties to even; the codes go to the row of the int8 cache
  *     and the scale to kv_scale[page * 64 + slot].  Dequantised value:
  *     code * scale, as the attention entry points read it.
+ *   fp8 cache (kv_dtype 2) [GITREAD, section "核心技术揭秘"]: the same with
+ *     scale = max_c |x_c| / 448 and code_c = the E4M3 value nearest to
+ *     x_c / scale (fp32 division), ties to the even mantissa, magnitudes
+ *     above 448 saturating to 448.  Dequantised value: e4m3(code) * scale.
+ *     Inputs must be finite.
  *
  *   kv_new          bf16 [total_new, 576] (latent | rope)
  *   cu_seqlens_new  int32 [batch+1], cu_seqlens_new[0] = 0, nondecreasing,
  *                   cu_seqlens_new[batch] = total_new
  *   start_pos       int32 [batch]: logical position of each request's first
  *                   new row (its cached length before the append)
- *   kv_cache        bf16 or int8 [num_pages, 64, 576], written in place
- *   kv_scale        fp32 [num_pages, 64] for an int8 cache (written), else NULL
+ *   kv_cache        bf16, int8 or fp8 [num_pages, 64, 576], written in place
+ *   kv_scale        fp32 [num_pages, 64] for an int8 or fp8 cache (written),
+ *                   else NULL
  *   page_table      int32 [batch, max_pages_per_req]
  *
  * Rows whose position falls outside 0 .. max_pages_per_req * 64 - 1 are not
@@ -211,7 +230,7 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
  * attention entry points).  Returns MLA_ERR_UNSUPPORTED for page_size != 64
  * or an unknown kv_dtype, MLA_ERR_INVALID for null pointers (when
  * total_new > 0), batch < 1, total_new < 0, max_pages_per_req < 1 or an
- * int8 cache without kv_scale.  total_new == 0 enqueues nothing.
+ * int8 or fp8 cache without kv_scale.  total_new == 0 enqueues nothing.
  */
 int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32_t* start_pos,
                   void* kv_cache, float* kv_scale, int kv_dtype, const int32_t* page_table,

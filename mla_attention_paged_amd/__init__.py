@@ -24,6 +24,7 @@ MLA_ERR_WORKSPACE = 3
 MLA_ERR_HIP = 4
 MLA_KV_BF16 = 0
 MLA_KV_INT8 = 1
+MLA_KV_FP8 = 2
 MLA_DIM_QK = 576
 MLA_DIM_V = 512
 MLA_PAGE_SIZE = 64

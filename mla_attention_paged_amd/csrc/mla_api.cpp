@@ -135,6 +135,10 @@ bool decode_shape(int batch, int num_heads, int max_q_len, int total_q) {
          (long long)batch * max_q_len == total_q;
 }
 
+bool known_dtype(int kv_dtype) {
+  return kv_dtype == MLA_KV_BF16 || kv_dtype == MLA_KV_INT8 || kv_dtype == MLA_KV_FP8;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,7 +158,7 @@ int mla_decode_plan(int batch, int num_heads, int q_len, int max_seq_len, int kv
                     int* phase1_groups, size_t* workspace_bytes) {
   if (!phase1_groups || !workspace_bytes) return MLA_ERR_INVALID;
   if (batch < 1 || num_heads < 1 || q_len < 1 || max_seq_len < q_len) return MLA_ERR_INVALID;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   if ((long long)q_len * num_heads > MLA_MAX_DECODE_ROWS) return MLA_ERR_UNSUPPORTED;
   DecodePlan p{};
   if (num_cus > 0) {
@@ -174,7 +178,7 @@ int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int tota
   *bytes_out = 0;
   if (batch < 1 || num_heads < 1 || max_q_len < 0 || total_q < max_q_len || max_seq_len < 1)
     return MLA_ERR_INVALID;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   int dev = 0, cus = 0;
   const int rc = device_cus(&dev, &cus);
   if (rc != MLA_OK) return rc;
@@ -201,8 +205,8 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
   if (!q || !kv_cache || !page_table || !seq_lens || !out || !lse) return MLA_ERR_INVALID;
   if (batch < 1 || q_len < 1 || num_heads < 1 || max_pages_per_req < 1 || max_seq_len < 1)
     return MLA_ERR_INVALID;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
-  if (kv_dtype == MLA_KV_INT8 && !kv_scale) return MLA_ERR_INVALID;
+  if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype != MLA_KV_BF16 && !kv_scale) return MLA_ERR_INVALID;
   if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
   if ((long long)q_len * num_heads > MLA_MAX_DECODE_ROWS) return MLA_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID;
@@ -254,8 +258,8 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
       max_seq_len < 1)
     return MLA_ERR_INVALID;
   if (total_q < max_q_len || max_seq_len < max_q_len) return MLA_ERR_INVALID;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
-  if (kv_dtype == MLA_KV_INT8 && !kv_scale) return MLA_ERR_INVALID;
+  if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype != MLA_KV_BF16 && !kv_scale) return MLA_ERR_INVALID;
   if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
   if (num_heads > MLA_MAX_HEADS) return MLA_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID;
@@ -299,11 +303,11 @@ int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32
                   void* kv_cache, float* kv_scale, int kv_dtype, const int32_t* page_table,
                   int max_pages_per_req, int batch, int total_new, int page_size, void* hip_stream) {
   if (batch < 1 || total_new < 0 || max_pages_per_req < 1) return MLA_ERR_INVALID;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
   if (total_new > 0 && (!kv_new || !cu_seqlens_new || !start_pos || !kv_cache || !page_table))
     return MLA_ERR_INVALID;
-  if (kv_dtype == MLA_KV_INT8 && !kv_scale) return MLA_ERR_INVALID;
+  if (kv_dtype != MLA_KV_BF16 && !kv_scale) return MLA_ERR_INVALID;
   if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)max_pages_per_req * MLA_PAGE_SIZE > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if (total_new == 0) return MLA_OK;
@@ -313,7 +317,8 @@ int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32
   a.cu = cu_seqlens_new;
   a.start_pos = start_pos;
   a.kv = static_cast<uint8_t*>(kv_cache);
-  a.kv_scale = kv_dtype == MLA_KV_INT8 ? kv_scale : nullptr;  // the kernel keys on it
+  a.kv_scale = kv_dtype != MLA_KV_BF16 ? kv_scale : nullptr;  // the kernel keys on it
+  a.code = kv_dtype;
   a.page_table = page_table;
   a.max_pages = max_pages_per_req;
   a.batch = batch;

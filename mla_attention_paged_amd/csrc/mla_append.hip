@@ -1,11 +1,16 @@
 // KV append: write the rows of new tokens into their requests' pages, as a
-// bf16 copy or as symmetric per-row INT8 codes with an fp32 scale.
+// bf16 copy or as symmetric per-row INT8 or FP8 (E4M3) codes with an fp32
+// scale.
 //
 // Sources (web pages on the TokenSpeed inference engine):
 //   [TALK] "构建面向 Agentic 推理的下一代 LLM 推理引擎", AICon 2026 talk
 //          transcript, section "Kernel：让 MLA 真正跑满 GPU": attention runs
 //          over a paged latent cache, one compressed row per token, and an
 //          INT8 latent cache is one way to cut decode's bandwidth.
+//   [GITREAD] "TokenSpeed 深度解析:把 LLM 推理压到"光速"意味着什么", section
+//          "核心技术揭秘": FP8 KV-cache quantisation.  Read as OCP E4M3
+//          (finite, largest magnitude 448), scale = max|x| / 448, values
+//          rounded to the nearest E4M3 value with ties to even, saturating.
 //
 // One wave per new row; the row's 72 16-byte chunks (8 values each) are
 // spread over the 64 lanes (lanes 0..7 take a second chunk).  The INT8 path
@@ -18,6 +23,28 @@
 namespace mla {
 
 constexpr int kAppendWaves = 4;  // rows per workgroup
+
+// E4M3 code of a finite fp32 value: nearest E4M3 value, ties to the even
+// mantissa, magnitudes above 448 saturating to 448.  For |q| >= 2^-6 (the
+// normal binades) |q| * 2^-120 is an exact fp32 whose exponent field is the
+// E4M3 exponent field and whose top 3 mantissa bits are the E4M3 mantissa;
+// rounding its low 20 bits to nearest-even on the bit pattern (a carry moves
+// into the exponent) gives the code's 7 magnitude bits.  Below 2^-6 the grid
+// is 2^-9: rint(|q| * 512) (exact scaling) is the subnormal mantissa, and
+// 8 lands on the smallest normal, whose code is also 8.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  uint32_t mag;
+  if (a < 0x1p-6f) {
+    mag = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const uint32_t u = __float_as_uint(a * 0x1p-120f);
+    const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    mag = min(r >> 20, 0x7Eu);
+  }
+  return sign | mag;
+}
 
 __global__ __launch_bounds__(kAppendWaves * 64) void kv_append(AppendArgs a) {
   const int lane = threadIdx.x & 63;
@@ -43,7 +70,9 @@ __global__ __launch_bounds__(kAppendWaves * 64) void kv_append(AppendArgs a) {
     return;
   }
 
-  // int8 cache: scale = max|x| / 127, code = clamp(rint(x / scale), -127, 127)
+  // int8 cache: scale = max|x| / 127, code = clamp(rint(x / scale), -127, 127);
+  // fp8 cache: scale = max|x| / 448, code = E4M3 nearest-even of x / scale
+  const bool fp8 = a.code == kCodeFp8;
   float x[2][8];
   float amax = 0.f;
 #pragma unroll
@@ -59,7 +88,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void kv_append(AppendArgs a) {
   }
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-  float scale = amax / 127.0f;
+  float scale = fp8 ? amax / 448.0f : amax / 127.0f;
   if (scale == 0.f) scale = 1.0f;
   uint8_t* dst = a.kv + pos * kI8RowBytes;
 #pragma unroll
@@ -68,8 +97,15 @@ __global__ __launch_bounds__(kAppendWaves * 64) void kv_append(AppendArgs a) {
     u32x2 packed = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float c = fminf(fmaxf(__builtin_rintf(x[k][e] / scale), -127.0f), 127.0f);
-      packed[e >> 2] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (e & 3));
+      const float qv = x[k][e] / scale;
+      uint32_t code;
+      if (fp8) {
+        code = e4m3_code(qv);
+      } else {
+        const float c = fminf(fmaxf(__builtin_rintf(qv), -127.0f), 127.0f);
+        code = (uint32_t)(int32_t)c & 0xffu;
+      }
+      packed[e >> 2] |= code << (8 * (e & 3));
     }
     *reinterpret_cast<u32x2*>(dst + 8 * (lane + 64 * k)) = packed;
   }
@@ -77,7 +113,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void kv_append(AppendArgs a) {
 }
 
 hipError_t launch_append(const AppendArgs& args, int kv_dtype, hipStream_t stream) {
-  (void)kv_dtype;  // the kernel keys on kv_scale (null for bf16)
+  (void)kv_dtype;  // the kernel keys on kv_scale (null for bf16) and args.code
   if (args.total_new <= 0) return hipSuccess;
   const int blocks = (args.total_new + kAppendWaves - 1) / kAppendWaves;
   hipLaunchKernelGGL(kv_append, dim3(blocks), dim3(kAppendWaves * 64), 0, stream, args);

@@ -143,140 +143,6 @@ __device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lan
   }
 }
 
-// Fill the window's page list: pages wlo .. wlo + n - 1 of the stream,
-// starting at request cb, page cj; returns the cursor after them.
-__device__ __forceinline__ void fill_window(const DecodeArgs& a, const Lens& lens, int n, int& cb, int& cj,
-                                            int* s_pid, int* s_req, int* s_rem, int nthreads) {
-  for (int k = threadIdx.x; k < n; k += nthreads) {
-    int b = cb, off = cj + k, Lc;
-    for (;;) {
-      Lc = lens(b);
-      const int np = (Lc + kPage - 1) / kPage;
-      if (off < np || b + 1 >= a.batch) break;
-      off -= np;
-      ++b;
-    }
-    off = min(off, a.max_pages - 1);  // never past the table, whatever the lengths say
-    s_pid[k] = a.page_table[(size_t)b * a.max_pages + off];
-    s_req[k] = b;
-    s_rem[k] = Lc - kPage * off;
-  }
-  int b = cb, off = cj + n;  // advance the cursor by n pages (uniform across the workgroup)
-  for (;;) {
-    const int np = (lens(b) + kPage - 1) / kPage;
-    if (off < np || b + 1 >= a.batch) break;
-    off -= np;
-    ++b;
-  }
-  cb = b;
-  cj = off;
-}
-
-// Phase one.  blockIdx.x: share of the page stream; blockIdx.y: block of 64
-// folded rows (requests with more than 64 rows use two).  I8: INT8 cache,
-// staged as codes + row scales and converted to exact bf16 per tile.
-template <bool I8>
-__global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1(DecodeArgs a) {
-  using R = Ring<I8>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[R::stages * R::stage_bytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[I8 ? kStageBytes : 16];
-  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[kWaves * 64];
-  MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
-  MLA_LDS uint8_t* const cvt = (MLA_LDS uint8_t*)cvt_raw;
-  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
-  __shared__ int s_pid[kWin], s_req[kWin], s_rem[kWin];
-  __shared__ int s_info[4];
-  __shared__ int s_len[kLenCache];
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int G = a.grid;
-  const int g = blockIdx.x;
-
-  if (w == 0) locate_share(a, g, lane, s_info, s_len);
-  __syncthreads();
-  const Lens lens{a, s_len};
-  const int seg_lo = s_info[0], seg_hi = s_info[1];
-  if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
-  int cb = s_info[2], cj = s_info[3];
-
-  // ---- this wave's 16 query rows (shared with wave w ^ 4) ----
-  const int half = w >> 2;
-  const int row = kBlockRows * blockIdx.y + 16 * (w & 3) + (lane & 15);
-  const bool wave_rows = kBlockRows * blockIdx.y + 16 * (w & 3) < a.rows;
-  const bool row_ok = row < a.rows;
-  const int draft = row_ok ? row / a.heads : 0;  // token index i of this row within its request
-  const int late = a.q_len - draft;              // row sees rows t <= L - late
-  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
-  const MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
-
-  RowState st;
-  bf16x8 qf[kQFrags];
-  int cur_b = -1;
-  // The first request's query loads start now, overlapping the tile-list
-  // fill and the first tile; the first tile's wait covers them.
-  int q_b = -1;  // request whose query fragments are loaded or in flight
-  if (wave_rows && cb < a.batch) {
-    issue_q(row_ok ? a.q + ((size_t)cb * a.rows + row) * kDqk : nullptr, lane, qf);
-    q_b = cb;
-  }
-
-  for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
-    const int n = min(kWin, seg_hi - wlo);
-    __syncthreads();  // the previous window's list and stages are no longer read
-    fill_window(a, lens, n, cb, cj, s_pid, s_req, s_rem, kWaves * 64);
-    __syncthreads();
-
-    // Tiles are half pages: tile k is half (k & 1) of window page k >> 1.
-    // R::stages - 1 tiles are in flight while one is consumed.
-    const int ntiles = 2 * n;
-    auto issue = [&](int k) {
-      const int p = k >> 1;
-      MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
-      if (I8)
-        stage_tile_i8<kWaves>(a.kv + (size_t)s_pid[p] * kI8PageBytes, a.kv_scale + (size_t)s_pid[p] * kPage,
-                              k & 1, s_rem[p], stage, w, lane);
-      else
-        stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, s_rem[p], stage, w, lane);
-    };
-    const int pre = min(R::stages - 1, ntiles);
-    for (int k = 0; k < pre; ++k) issue(k);
-    for (int k = 0; k < ntiles; ++k) {
-      const int p = k >> 1;
-      const int b = s_req[p];
-      const int rem = s_rem[p] - kTileRows * (k & 1);  // request rows from this tile's start
-      if (b != cur_b) {
-        if (cur_b >= 0 && wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
-        cur_b = b;
-        if (wave_rows) {
-          if (b != q_b) load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
-          q_b = -1;
-          reset_state(st);
-        }
-      }
-      wait_tile<kWaves, R::loads>(min(R::stages - 2, ntiles - 1 - k), w);  // this wave's loads of tile k landed
-      lds_barrier();  // ... every wave's; tile k-1's stage (and the converted tile) is free
-      if (k + R::stages - 1 < ntiles) issue(k + R::stages - 1);
-      if (rem > 0) {  // uniform: every wave takes part in the barriers below
-        const MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
-        const MLA_LDS uint8_t* tile = stage;
-        if (I8) {
-          convert_i8_tile(stage, cvt, threadIdx.x, kWaves * 64);
-          lds_write_barrier();
-          tile = cvt;
-        }
-        if (wave_rows)
-          attend_tile<I8>(tile, qf, rem - late, a.scale_log2, lane, half, xmine, xpart, st,
-                          reinterpret_cast<const MLA_LDS float*>(stage + kI8CodeBytes));
-        else
-          lds_write_barrier();
-      }
-    }
-  }
-  if (wave_rows) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
-}
-
-
 // Fill the window's tile list: the valid tiles (half pages holding at least
 // one of their request's rows) of pages wlo .. wlo + n - 1 of the stream,
 // starting at request cb, page cj, in stream order.  Tile t: page s_pid[t],
@@ -444,6 +310,139 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   if (wave_rows && cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
 }
 
+// Phase one for an INT8 or FP8 cache (CODE), software-pipelined like the
+// bf16 kernel.  The codes stream through three LDS stages (two tiles in
+// flight: a code tile is half the bytes of a bf16 one); step t of a window
+// waits for the codes of tile t, passes barrier A (every wave is done with
+// step t - 1), starts tile t + 2, converts tile t to exact bf16 in one of two
+// converted buffers (its 32 row scales beside it), passes barrier C, then
+// computes the scores of tile t from its converted buffer while the softmax
+// and value product of tile t - 1 use the other buffer and its scales.  The
+// score halves travel between partner waves through a double-buffered slot,
+// so two barriers per step suffice.
+constexpr int kCStages = 3;
+
+template <int CODE>
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t codes_raw[kCStages * kI8StageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) float tsc_raw[2 * kTileRows];
+  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[2 * kWaves * 64];
+  MLA_LDS uint8_t* const codes = (MLA_LDS uint8_t*)codes_raw;
+  MLA_LDS uint8_t* const cvt = (MLA_LDS uint8_t*)cvt_raw;
+  MLA_LDS float* const tsc = (MLA_LDS float*)tsc_raw;
+  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
+  __shared__ int s_pid[2 * kWin], s_req[2 * kWin], s_rem[2 * kWin];
+  __shared__ int s_info[5];
+  __shared__ int s_len[kLenCache];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = blockIdx.x;
+  if (w == 0) locate_share(a, g, lane, s_info, s_len);
+  __syncthreads();
+  const Lens lens{a, s_len};
+  const int seg_lo = s_info[0], seg_hi = s_info[1];
+  if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
+  int cb = s_info[2], cj = s_info[3];
+
+  const int half = w >> 2;
+  const int row = kBlockRows * blockIdx.y + 16 * (w & 3) + (lane & 15);
+  const bool wave_rows = kBlockRows * blockIdx.y + 16 * (w & 3) < a.rows;
+  const bool row_ok = row < a.rows;
+  const int draft = row_ok ? row / a.heads : 0;
+  const int late = a.q_len - draft;  // row sees rows t <= L - late
+  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
+  MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
+  auto code_stage = [&](int t) { return codes + (t % kCStages) * kI8StageBytes; };
+  auto cvt_of = [&](int t) { return cvt + (t & 1) * kStageBytes; };
+  auto tsc_of = [&](int t) { return tsc + (t & 1) * kTileRows; };
+
+  RowState st;
+  bf16x8 qf[kQFrags];
+  int cur_b = -1;
+  int q_b = -1;  // request whose query fragments are loaded or in flight
+  if (wave_rows && cb < a.batch) {
+    issue_q(row_ok ? a.q + ((size_t)cb * a.rows + row) * kDqk : nullptr, lane, qf);
+    q_b = cb;
+  }
+
+  for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
+    const int n = min(kWin, seg_hi - wlo);
+    __syncthreads();  // the previous window's list, stages and buffers are no longer read
+    fill_window_tiles(a, lens, n, cb, cj, s_pid, s_req, s_rem, &s_info[4], w, lane);
+    __syncthreads();
+    const int N = s_info[4];
+    auto issue = [&](int t) {
+      stage_tile_i8<kWaves>(a.kv + (size_t)s_pid[t] * kI8PageBytes, a.kv_scale + (size_t)s_pid[t] * kPage,
+                            s_req[t] & 1, s_rem[t] + kTileRows * (s_req[t] & 1), code_stage(t), w, lane);
+    };
+    issue(0);
+    if (N > 1) issue(1);
+    int issued = N > 1 ? 2 : 1;
+    auto wait_for = [&](int t) {  // codes of tile t landed; tile t + 1 may stay in flight
+      if (t + 1 < issued) wait_tile<kWaves, kI8StageLoads>(1, w); else wait_vmcnt<0>();
+    };
+    // steps up to barrier C: tile t's codes in, tile t + 2 started, tile t converted
+    auto bring = [&](int t) {
+      wait_for(t);
+      lds_write_barrier();  // A: codes of t visible; every wave is done with step t - 1
+      if (issued < N) {
+        issue(issued);
+        ++issued;
+      }
+      convert_code_tile_sc<CODE>(code_stage(t), cvt_of(t), tsc_of(t), threadIdx.x);
+      lds_write_barrier();  // C: tile t converted
+    };
+    for (int t0 = 0; t0 < N;) {
+      const int b = s_req[t0] >> 1;
+      int t1 = t0 + 1;
+      while (t1 < N && (s_req[t1] >> 1) == b) ++t1;
+      if (wave_rows && b != cur_b) {
+        if (cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
+        if (b != q_b) load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+        q_b = -1;
+        reset_state(st);
+      }
+      cur_b = b;
+      // first step: scores only
+      bring(t0);
+      f32x4 s_prev = {0.f, 0.f, 0.f, 0.f};
+      if (wave_rows) {
+        s_prev = tile_scores(cvt_of(t0), qf, lane, half);
+        xmine[(t0 & 1) * kWaves * 64] = s_prev;
+      }
+      int prev_lim = s_rem[t0] - late;
+      for (int t = t0 + 1; t < t1; ++t) {
+        bring(t);
+        const int lim = s_rem[t] - late;
+        if (wave_rows) {
+          const f32x4 other = xpart[((t - 1) & 1) * kWaves * 64];
+          const f32x4 lo = half == 0 ? s_prev : other;
+          const f32x4 hi = half == 0 ? other : s_prev;
+          s_prev = tile_step<true>(cvt_of(t), cvt_of(t - 1), qf, lo, hi, prev_lim, a.scale_log2, lane, half, st,
+                                   tsc_of(t - 1));
+          xmine[(t & 1) * kWaves * 64] = s_prev;
+        }
+        prev_lim = lim;
+      }
+      // last tile of the segment
+      lds_write_barrier();
+      if (wave_rows) {
+        const f32x4 other = xpart[((t1 - 1) & 1) * kWaves * 64];
+        const f32x4 lo = half == 0 ? s_prev : other;
+        const f32x4 hi = half == 0 ? other : s_prev;
+        float alpha;
+        const bf16x8 pb = tile_softmax<true>(lo, hi, prev_lim, a.scale_log2, lane, st, alpha, tsc_of(t1 - 1));
+        rescale_o(st, alpha);
+        tile_values(cvt_of(t1 - 1), pb, lane, half, st);
+      }
+      t0 = t1;
+    }
+  }
+  if (wave_rows && cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
+}
+
 // Phase two: per (request, row), reduce the partials of the workgroups
 // whose shares intersect the request: lse = log2-sum-exp of the partial
 // lses, out = sum_s 2^(lse_s - lse) o_s.  One workgroup per (row, quarter of
@@ -545,7 +544,11 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream) {
   const int row_blocks = (args.rows + kBlockRows - 1) / kBlockRows;
   if (kv_dtype == 1)
-    hipLaunchKernelGGL(decode_phase1<true>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL(decode_phase1_codes<kCodeInt8>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream,
+                       args);
+  else if (kv_dtype == 2)
+    hipLaunchKernelGGL(decode_phase1_codes<kCodeFp8>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream,
+                       args);
   else
     hipLaunchKernelGGL(decode_phase1_pipe, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   hipError_t e = hipGetLastError();

@@ -65,7 +65,7 @@ static_assert(kStageLoads * 64 == kTileSlots, "a tile is a whole number of wave-
 constexpr int kStageBytes = kStageLoads * 1024;         // 37888
 constexpr int kStages = 4;                     // ring depth: 3 tiles in flight
 
-// INT8 cache: a stage holds the 32 rows' codes (576 B each, unpadded: they
+// INT8 / FP8 cache: a stage holds the 32 rows' codes (576 B each, unpadded: they
 // are only read by the conversion pass, 16 contiguous bytes per lane) and
 // their 32 fp32 scales.  Codes are half the bytes of a bf16 row, so the ring
 // is deeper (five tiles in flight) to keep as many bytes in flight.
@@ -210,7 +210,7 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ page, int
   }
 }
 
-// INT8 tile staging: loads 0..17 bring the 32 rows' codes (16-byte chunk s
+// INT8 / FP8 tile staging: loads 0..17 bring the 32 rows' codes (16-byte chunk s
 // of the tile is row s / 36, bytes 16 (s % 36) ..), load 18 brings the 32
 // scales with lanes 0..7.  Rows at or past `rem` re-read row 0's codes; their
 // scales are fetched as they are and never used unmasked.
@@ -242,22 +242,67 @@ __device__ __forceinline__ unsigned i8pair_to_bf16(unsigned x, int k) {
   return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
 }
 
-// Convert a staged INT8 tile's codes into exact bf16 values in `cvt`, laid
-// out like a staged bf16 tile (pitch 1184), cooperatively by all threads.
-__device__ __forceinline__ void convert_i8_tile(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt, int tid,
-                                                int nthreads) {
-  for (int c = tid; c < kI8CodeBytes / 16; c += nthreads) {
-    const int t = c / 36, j = c - 36 * t;
-    const u32x4 x = *reinterpret_cast<const MLA_LDS u32x4*>(stage + 16 * c);
-    u32x4 lo, hi;
-    lo[0] = i8pair_to_bf16(x[0], 0); lo[1] = i8pair_to_bf16(x[0], 1);
-    lo[2] = i8pair_to_bf16(x[1], 0); lo[3] = i8pair_to_bf16(x[1], 1);
-    hi[0] = i8pair_to_bf16(x[2], 0); hi[1] = i8pair_to_bf16(x[2], 1);
-    hi[2] = i8pair_to_bf16(x[3], 0); hi[3] = i8pair_to_bf16(x[3], 1);
-    MLA_LDS u32x4* dst = reinterpret_cast<MLA_LDS u32x4*>(cvt + t * kLdsPitch + 32 * j);
-    dst[0] = lo;
-    dst[1] = hi;
+// Two E4M3 codes (bytes 2k, 2k+1 of x) as two exact bf16 values: gfx950's
+// packed FP8 -> fp32 conversion (it decodes the OCP E4M3 format: checked on
+// the GPU against every code byte), then the upper halves of the two fp32
+// values, which are exact bf16 (E4M3 values have 4 significant bits).
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+template <int K>
+__device__ __forceinline__ unsigned fp8pair_to_bf16(unsigned x) {
+  const f32x2_cvt f = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, K != 0);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// Cache code formats of the scaled caches.
+constexpr int kCodeInt8 = 1;
+constexpr int kCodeFp8 = 2;
+
+template <int CODE, int K>
+__device__ __forceinline__ unsigned codepair_to_bf16(unsigned x) {
+  return CODE == kCodeFp8 ? fp8pair_to_bf16<K>(x) : i8pair_to_bf16(x, K);
+}
+
+// Convert a staged tile's codes (INT8 or E4M3) into exact bf16 values in
+// `cvt`, laid out like a staged bf16 tile (pitch 1184), cooperatively by the
+// workgroup's kWaves * 64 threads: thread i converts 16-byte chunks i, i + 512
+// and (i < 128) i + 1024 of the 1152, all of whose loads are issued before
+// the first conversion (one LDS round trip instead of three).
+template <int CODE>
+__device__ __forceinline__ void convert_code_tile(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt, int tid) {
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kChunks = kI8CodeBytes / 16;
+  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
+  static_assert(kPer == 3 && kChunks > 2 * kThreads, "chunk split");
+  u32x4 x[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (i < kPer - 1 || tid + i * kThreads < kChunks)
+      x[i] = *reinterpret_cast<const MLA_LDS u32x4*>(stage + 16 * (tid + i * kThreads));
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = tid + i * kThreads;
+    if (i < kPer - 1 || c < kChunks) {
+      const int t = c / 36, j = c - 36 * t;
+      u32x4 lo, hi;
+      lo[0] = codepair_to_bf16<CODE, 0>(x[i][0]); lo[1] = codepair_to_bf16<CODE, 1>(x[i][0]);
+      lo[2] = codepair_to_bf16<CODE, 0>(x[i][1]); lo[3] = codepair_to_bf16<CODE, 1>(x[i][1]);
+      hi[0] = codepair_to_bf16<CODE, 0>(x[i][2]); hi[1] = codepair_to_bf16<CODE, 1>(x[i][2]);
+      hi[2] = codepair_to_bf16<CODE, 0>(x[i][3]); hi[3] = codepair_to_bf16<CODE, 1>(x[i][3]);
+      MLA_LDS u32x4* dst = reinterpret_cast<MLA_LDS u32x4*>(cvt + t * kLdsPitch + 32 * j);
+      dst[0] = lo;
+      dst[1] = hi;
+    }
   }
+}
+
+// The same, and the tile's 32 row scales copied to `tsc` (for the pipelined
+// core, which reads a tile's scales one step after its codes are gone).
+template <int CODE>
+__device__ __forceinline__ void convert_code_tile_sc(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt,
+                                                     MLA_LDS float* tsc, int tid) {
+  convert_code_tile<CODE>(stage, cvt, tid);
+  if (tid < kTileRows / 4)
+    reinterpret_cast<MLA_LDS f32x4*>(tsc)[tid] = reinterpret_cast<const MLA_LDS f32x4*>(stage + kI8CodeBytes)[tid];
 }
 
 // Per-wave attention state: 16 query rows x 256 value columns.
@@ -486,14 +531,24 @@ __device__ __forceinline__ f32x4 tile_scores(const MLA_LDS uint8_t* tile, const 
 // one branch-free block that can be interleaved with the next tile's score
 // MFMAs.  Returns the probabilities in the B-operand layout of the value
 // product.
+template <bool SCALED = false>
 __device__ __forceinline__ bf16x8 tile_softmax(f32x4 lo, f32x4 hi, int lim, float scale_log2, int lane,
-                                               RowState& st, float& alpha) {
+                                               RowState& st, float& alpha, const MLA_LDS float* tsc = nullptr) {
   const int g = lane >> 4;
+  f32x4 sc_lo = {1.f, 1.f, 1.f, 1.f}, sc_hi = {1.f, 1.f, 1.f, 1.f};
+  if (SCALED) {
+    sc_lo = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 4 * g);
+    sc_hi = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 16 + 4 * g);
+  }
   float s[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     float v0 = lo[e] * scale_log2, v1 = hi[e] * scale_log2;
+    if (SCALED) {
+      v0 *= sc_lo[e];
+      v1 *= sc_hi[e];
+    }
     v0 = 4 * g + e <= lim ? v0 : -INFINITY;
     v1 = 16 + 4 * g + e <= lim ? v1 : -INFINITY;
     s[e] = v0;
@@ -514,8 +569,19 @@ __device__ __forceinline__ bf16x8 tile_softmax(f32x4 lo, f32x4 hi, int lim, floa
   }
   st.l = st.l * alpha + psum;
   bf16x8 pb;
+  if (SCALED) {
+    // the row sum takes the unscaled probabilities; the value product the
+    // probability times the row's scale (a select on masked rows, whose scale
+    // may be non-finite)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
+    for (int e = 0; e < 4; ++e) {
+      pb[e] = (__bf16)(4 * g + e <= lim ? s[e] * sc_lo[e] : 0.f);
+      pb[4 + e] = (__bf16)(16 + 4 * g + e <= lim ? s[4 + e] * sc_hi[e] : 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
+  }
   return pb;
 }
 
@@ -561,12 +627,14 @@ __device__ __forceinline__ void tile_values(const MLA_LDS uint8_t* tile, bf16x8 
 // softmax of tile k-1 interleaved into the MFMA chain, then the value
 // product of tile k-1.  Scores and softmax are independent and in one
 // basic block, so the VALU work can issue while the MFMAs execute.
+template <bool SCALED = false>
 __device__ __forceinline__ f32x4 tile_step(const MLA_LDS uint8_t* tile_k, const MLA_LDS uint8_t* tile_prev,
                                            const bf16x8 (&qf)[kQFrags], f32x4 lo, f32x4 hi, int lim,
-                                           float scale_log2, int lane, int half, RowState& st) {
+                                           float scale_log2, int lane, int half, RowState& st,
+                                           const MLA_LDS float* tsc_prev = nullptr) {
   const f32x4 sc = tile_scores(tile_k, qf, lane, half);
   float alpha;
-  const bf16x8 pb = tile_softmax(lo, hi, lim, scale_log2, lane, st, alpha);
+  const bf16x8 pb = tile_softmax<SCALED>(lo, hi, lim, scale_log2, lane, st, alpha, tsc_prev);
   rescale_o(st, alpha);
   tile_values(tile_prev, pb, lane, half, st);
   return sc;

@@ -66,6 +66,7 @@ struct AppendArgs {
   int max_pages;
   int batch;
   int total_new;
+  int code;                   // scaled caches: 1 INT8, 2 FP8 (E4M3)
 };
 
 struct DecodePlan {

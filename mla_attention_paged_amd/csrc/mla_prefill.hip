@@ -146,10 +146,11 @@ __device__ __forceinline__ void store_rows(const PrefillArgs& a, const RowState&
   }
 }
 
-// INT8 cache: the lockstep core.  Every tile is converted to bf16 in LDS by
-// all waves after its barrier, then scored, normalised and accumulated
-// before the next tile starts; R::stages - 1 tiles are in flight.
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_i8(PrefillArgs a) {
+// INT8 or FP8 cache (CODE): the lockstep core.  Every tile is converted to
+// bf16 in LDS by all waves after its barrier, then scored, normalised and
+// accumulated before the next tile starts; R::stages - 1 tiles are in flight.
+template <int CODE>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_codes(PrefillArgs a) {
   using R = Ring<true>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[R::stages * R::stage_bytes];
   __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[kStageBytes];
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_i8(PrefillA
         lds_barrier();
         if (k + R::stages - 1 < ntiles) issue(k + R::stages - 1);
         const MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
-        convert_i8_tile(stage, cvt, threadIdx.x, kWaves * 64);
+        convert_code_tile<CODE>(stage, cvt, threadIdx.x);
         lds_write_barrier();
         if (x.wave_rows) {
           const int lim = x.row_ok ? x.vis_last - t0 : -1;
@@ -333,7 +334,9 @@ hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (kv_dtype == 1)
-    hipLaunchKernelGGL(prefill_persistent_i8, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL(prefill_persistent_codes<kCodeInt8>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
+  else if (kv_dtype == 2)
+    hipLaunchKernelGGL(prefill_persistent_codes<kCodeFp8>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   else
     hipLaunchKernelGGL(prefill_persistent_bf16, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();

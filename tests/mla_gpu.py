@@ -22,7 +22,7 @@ def dev_cache(cache, device="cuda"):
     else:
         data = torch.from_numpy(np.ascontiguousarray(cache.data)).to(device)
         scale = torch.from_numpy(np.ascontiguousarray(cache.scale)).to(device)
-        kind = mla.MLA_KV_INT8
+        kind = mla.MLA_KV_INT8 if cache.kv_dtype == "int8" else mla.MLA_KV_FP8
     pt = torch.from_numpy(np.ascontiguousarray(cache.page_table)).to(device)
     return data, scale, kind, pt
 

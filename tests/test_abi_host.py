@@ -60,8 +60,9 @@ def _decode_rc(lib, **kw):
     (dict(heads=0), mla.MLA_ERR_INVALID),
     (dict(page=32), mla.MLA_ERR_UNSUPPORTED),
     (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
-    (dict(kind=2), mla.MLA_ERR_UNSUPPORTED),
+    (dict(kind=3), mla.MLA_ERR_UNSUPPORTED),
     (dict(kind=1), mla.MLA_ERR_INVALID),            # int8 without scales
+    (dict(kind=2), mla.MLA_ERR_INVALID),            # fp8 without scales
     (dict(q_len=9, heads=16), mla.MLA_ERR_UNSUPPORTED),  # 144 folded rows
     (dict(scale_f=0.0), mla.MLA_ERR_INVALID),
     (dict(scale_f=float("nan")), mla.MLA_ERR_INVALID),
@@ -85,6 +86,8 @@ def test_prefill_argument_checks(lib):
     assert rc(cu=None) == mla.MLA_ERR_INVALID
     assert rc(prefix=None) == mla.MLA_ERR_INVALID
     assert rc(heads=129) == mla.MLA_ERR_UNSUPPORTED
+    assert rc(kind=2) == mla.MLA_ERR_INVALID             # fp8 without scales
+    assert rc(kind=3) == mla.MLA_ERR_UNSUPPORTED
     assert rc(page=16) == mla.MLA_ERR_UNSUPPORTED
     assert rc(tq=5, mq=6) == mla.MLA_ERR_INVALID
     assert rc(maxp=63) == mla.MLA_ERR_INVALID
@@ -123,6 +126,7 @@ def test_workspace_size_argument_checks(lib):
     assert lib.mla_splitkv_workspace_size(0, 16, 4, 16, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
     assert lib.mla_splitkv_workspace_size(4, 16, 4, 3, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
     assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 7, ctypes.byref(out)) == mla.MLA_ERR_UNSUPPORTED
+    assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 2, ctypes.byref(out)) == mla.MLA_OK
 
 
 def _append_rc(lib, **kw):
@@ -143,7 +147,8 @@ def _append_rc(lib, **kw):
     (dict(total=-1), mla.MLA_ERR_INVALID),
     (dict(maxp=0), mla.MLA_ERR_INVALID),
     (dict(kind=1), mla.MLA_ERR_INVALID),            # int8 without scales
-    (dict(kind=2), mla.MLA_ERR_UNSUPPORTED),
+    (dict(kind=2), mla.MLA_ERR_INVALID),            # fp8 without scales
+    (dict(kind=3), mla.MLA_ERR_UNSUPPORTED),
     (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
     (dict(total=0, new=None, kv=None), mla.MLA_OK),  # nothing to write, nothing enqueued
 ])

@@ -1,6 +1,6 @@
 """KV append parity: the HIP kernel through the C ABI against the oracle, bit-exact (GPU).
 
-bf16 rows must land unchanged and INT8 codes and scales must equal the
+bf16 rows must land unchanged and INT8 / FP8 codes and scales must equal the
 oracle's to the bit; nothing outside the written slots may change."""
 import numpy as np
 import pytest
@@ -17,6 +17,10 @@ pytestmark = pytest.mark.gpu
 def _fresh_cache(rng, kv_dtype, num_pages):
     if kv_dtype == "bf16":
         return rng.integers(0, 1 << 16, size=(num_pages, 64, 576), dtype=np.uint16), None
+    if kv_dtype == "fp8":
+        codes = rng.integers(0, 256, size=(num_pages, 64, 576), dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x7E
+        return codes, (rng.random((num_pages, 64), dtype=np.float32) + np.float32(0.5))
     return (rng.integers(-127, 128, size=(num_pages, 64, 576), dtype=np.int8),
             (rng.random((num_pages, 64), dtype=np.float32) + np.float32(0.5)))
 
@@ -30,7 +34,7 @@ def run_append(new_bits, cu, start, cache, scale, kv_dtype, pt):
     else:
         kv = torch.from_numpy(np.ascontiguousarray(cache)).cuda()
         sc = torch.from_numpy(np.ascontiguousarray(scale)).cuda()
-        kind = mla.MLA_KV_INT8
+        kind = mla.MLA_KV_INT8 if kv_dtype == "int8" else mla.MLA_KV_FP8
     new = dev_bf16(np.ascontiguousarray(new_bits).reshape(-1, 576))
     cu_d = torch.from_numpy(np.asarray(cu, np.int32)).cuda()
     st_d = torch.from_numpy(np.asarray(start, np.int32)).cuda()
@@ -46,11 +50,11 @@ def _check(new_bits, cu, start, cache, scale, kv_dtype, pt):
     got, got_sc = run_append(new_bits, cu, start, cache, scale, kv_dtype, pt)
     ref, ref_sc = oracle.kv_append(new_bits, cu, start, cache, scale, kv_dtype, pt)
     assert np.array_equal(got, ref)
-    if kv_dtype == "int8":
+    if kv_dtype != "bf16":
         assert np.array_equal(got_sc.view(np.uint32), ref_sc.view(np.uint32))
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
 def test_append_ragged_matches_oracle(kv_dtype):
     rng = np.random.default_rng(31)
     batch, max_pages = 4, 6
@@ -64,7 +68,7 @@ def test_append_ragged_matches_oracle(kv_dtype):
     _check(new, cu, start, cache, scale, kv_dtype, pt)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
 def test_append_edge_rows(kv_dtype):
     """Rows past the page table are dropped; zero rows, ties and huge / tiny magnitudes."""
     rng = np.random.default_rng(32)
@@ -86,7 +90,7 @@ def test_append_edge_rows(kv_dtype):
     _check(new, cu, start, cache, scale, kv_dtype, pt)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
 def test_append_prefill_workload_tokens(kv_dtype):
     """The long-prefix prefill's 8,629 new tokens, appended at their prefix positions."""
     case = synth.make_workload(3)
@@ -143,3 +147,44 @@ def test_append_then_decode_int8():
     out, lse = host(*run_decode(case8))
     ref_out, ref_lse = oracle.decode(case8)
     assert_close(out, lse, ref_out, ref_lse, "append-quantised int8 decode")
+
+
+def test_append_fp8_rounding_edges():
+    """max|x| = 448 makes the scale exactly 1, so the codes are the E4M3 rounding of the
+    inputs themselves: ties to even in the normal and subnormal ranges, values that round
+    up into the next binade, the smallest subnormals, signed zeros."""
+    pt = np.arange(2, dtype=np.int32).reshape(1, 2)
+    cache, scale = _fresh_cache(np.random.default_rng(34), "fp8", 2)
+    x = np.zeros((3, 576), np.float32)
+    vals = [448.0, 17.0, 19.0, -17.0, -19.0, 2.0 ** -10, 3 * 2.0 ** -10, 5 * 2.0 ** -10, -3 * 2.0 ** -10,
+            2.0 ** -6 - 2.0 ** -10, 31.0, 30.0, 1.0625, 1.1875, 240.0, 416.0, 432.0, -0.0, 2.0 ** -9,
+            0.9375 * 2.0 ** -6, 15.5, 0.09375]
+    x[0, :len(vals)] = vals
+    x[1] = x[0] * np.float32(-1.0)
+    x[2, 0] = 448.0
+    x[2, 1:] = np.random.default_rng(35).uniform(-448, 448, 575).astype(np.float32)
+    new = synth.bf16_bits(x)
+    assert np.array_equal(synth.bf16_to_f32(new)[0, :len(vals)], x[0, :len(vals)])   # exact inputs
+    cu = np.array([0, 3], np.int32)
+    _check(new, cu, np.array([5], np.int32), cache, scale, "fp8", pt)
+
+
+def test_append_then_decode_fp8():
+    """Quantise a bf16 cache to FP8 with the append kernel, then decode it: matches the
+    oracle on the oracle-quantised cache (which is bit-identical)."""
+    case = synth.make_decode_case(543, batch=2, heads=16, q_len=4, seq_lens=[700, 257])
+    c = case.cache
+    rows = _logical_rows(c)
+    cu = np.concatenate([[0], np.cumsum(c.kv_lens)]).astype(np.int32)
+    num_pages = c.data.shape[0]
+    codes0 = np.zeros((num_pages, 64, 576), np.uint8)
+    scale0 = np.ones((num_pages, 64), np.float32)
+    got, got_sc = run_append(rows, cu, np.zeros(2, np.int32), codes0, scale0, "fp8", c.page_table)
+    ref, ref_sc = oracle.kv_append(rows, cu, np.zeros(2, np.int32), codes0, scale0, "fp8", c.page_table)
+    assert np.array_equal(got, ref) and np.array_equal(got_sc.view(np.uint32), ref_sc.view(np.uint32))
+    case8 = synth.DecodeCase(case.batch, case.heads, case.q_len, case.q,
+                             synth.PagedCache("fp8", got, got_sc, c.page_table, c.kv_lens, c.poison_page),
+                             max_seq_len=case.max_seq_len)
+    out, lse = host(*run_decode(case8))
+    ref_out, ref_lse = oracle.decode(case8)
+    assert_close(out, lse, ref_out, ref_lse, "append-quantised fp8 decode")

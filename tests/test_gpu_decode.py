@@ -297,6 +297,59 @@ def test_decode_int8_needle():
     assert_close(out, lse, ref_out, ref_lse, "int8 needle")
 
 
+# ---------------------------------------------------------------- FP8 (E4M3) cache
+
+FP8_SMALL = [
+    (521, 1, 16, 1, [256]),
+    (522, 3, 16, 4, [65, 300, 1000]),
+    (523, 4, 32, 2, [33, 64, 127, 2500]),
+    (524, 2, 128, 1, [700, 90]),
+    (525, 1, 16, 4, [4]),
+]
+
+
+@pytest.mark.parametrize("seed,batch,heads,q_len,lens", FP8_SMALL, ids=[str(s[0]) for s in FP8_SMALL])
+def test_decode_fp8_matches_oracle(seed, batch, heads, q_len, lens):
+    case = synth.make_decode_case(seed, batch, heads, q_len, seq_lens=lens, kv_dtype="fp8")
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, f"fp8 seed {seed}")
+
+
+def test_decode_fp8_every_code():
+    """Rows that hold every finite E4M3 code (subnormals, both zeros, +-448): the widening
+    to bf16 must be exact for each of them."""
+    case = synth.make_decode_case(526, 1, 16, 1, seq_lens=[300], kv_dtype="fp8")
+    c = case.cache
+    finite = np.array([v for v in range(256) if (v & 0x7F) != 0x7F], np.uint8)
+    for t in range(300):
+        c.data[c.page_table[0, t // 64], t % 64] = np.roll(np.resize(finite, 576), 7 * t)
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, "fp8 every code")
+
+
+def test_decode_fp8_nan_scale_poison_has_no_effect():
+    lens = [70, 129, 1]
+    a = synth.make_decode_case(527, 3, 16, 1, seq_lens=lens, max_seq_len=400, kv_dtype="fp8")
+    b = synth.make_decode_case(527, 3, 16, 1, seq_lens=lens, max_seq_len=400, kv_dtype="fp8",
+                               poison=synth.POISON_NAN)
+    oa, la = run_decode(a)
+    ob, lb = run_decode(b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)) and torch.equal(la, lb)
+    assert torch.isfinite(ob.float()).all()
+
+
+def test_decode_fp8_long_sampled():
+    """Two 64K-row FP8 requests, 4 drafts x 16 heads; the oracle evaluates two tokens."""
+    case = synth.make_decode_case(528, 2, 16, 4, seq_lens=[65536, 65536], kv_dtype="fp8")
+    out, lse = host(*run_decode(case))
+    toks = [0, 7]
+    ref_out, ref_lse = oracle.decode(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
+    assert_close(out[toks], lse[toks], ref_out, ref_lse, "fp8 64K")
+
+
 def test_decode_workload4_sampled():
     """Full-size INT8 decode (8 requests x 4 drafts x 16 heads, 262,144 rows each); the
     oracle evaluates one draft of two requests, all heads."""

@@ -98,3 +98,14 @@ def test_prefill_int8_matches_oracle(seed, heads, prefix, new):
     ref_out, ref_lse = oracle.prefill(case)
     T = case.total_q()
     assert_close(out[:T], lse[:T], ref_out, ref_lse, f"int8 seed {seed}")
+
+
+@pytest.mark.parametrize("seed,heads,prefix,new", [(430, 16, [100, 0, 64], [5, 70, 1]),
+                                                   (431, 128, [77, 10], [3, 2]),
+                                                   (432, 16, [1000, 63], [17, 9])])
+def test_prefill_fp8_matches_oracle(seed, heads, prefix, new):
+    case = synth.make_prefill_case(seed, heads, prefix_lens=prefix, new_lens=new, kv_dtype="fp8")
+    out, lse = host(*run_prefill(case))
+    ref_out, ref_lse = oracle.prefill(case)
+    T = case.total_q()
+    assert_close(out[:T], lse[:T], ref_out, ref_lse, f"fp8 seed {seed}")
