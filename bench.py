@@ -202,6 +202,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the ragged-draft decode leg (1..4 drafts per request) on the 64K decode shape")
     ap.add_argument("--no-scaled", action="store_true",
                     help="skip the INT8 / FP8 cache decode leg on the 64K decode shape")
     ap.add_argument("--copies", type=int, default=3)
@@ -316,6 +318,39 @@ def main() -> int:
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
         }
+
+    # ---------------- ragged drafts: the 64K decode shape with 1, 2, 3, 4 drafts ----------------
+    if not args.no_varlen:
+        qls = np.array([1, 2, 3, 4], np.int32)
+        vcase = synth.make_prefill_case(2, H, prefix_lens=case.seq_lens - qls, new_lens=qls)
+        vin = prefill_inputs(vcase)
+        vT = vcase.total_q()
+        vlens = torch.from_numpy(vcase.cache.kv_lens.copy()).cuda()
+        vkv = [vin["kv"]] + [vin["kv"].clone() for _ in range(max(0, args.copies - 1))]
+        vws_b = mla.mla_splitkv_workspace_size(vcase.batch, H, 4, vT, vcase.max_seq_len, vin["kind"])
+        vws = torch.empty(max(vws_b, 1), dtype=torch.uint8, device="cuda")
+        vout = torch.empty((vT, H, 512), dtype=torch.bfloat16, device="cuda")
+        vlse = torch.empty((vT, H), dtype=torch.float32, device="cuda")
+
+        def make_vcall(kv):
+            def call():
+                mla.mla_decode_varlen(vin["q"], vin["cu"], kv, vin["scale"], vin["kind"], vin["pt"],
+                                      vcase.cache.max_pages, vlens, vcase.batch, vT, 4, H, 64, vcase.max_seq_len,
+                                      vcase.softmax_scale, vout, vlse, vws, vws.numel(), stream)
+            return call
+
+        vsteps = max(20, args.steps // 2)
+        vms = time_calls([make_vcall(kv) for kv in vkv], stream, max(10, args.warmup // 2), vsteps) / vsteps
+        L = vcase.cache.kv_lens.astype(np.int64)
+        vbytes = int(L.sum() * 1152 + vT * H * (576 * 2 + 512 * 2 + 4) + int(((L + 63) // 64).sum()) * 4
+                     + vcase.batch * 8)
+        result["varlen_decode"] = {"workload": "decode_b4_h16_L64K, drafts 1/2/3/4 per request (mla_decode_varlen)",
+                                   "us_per_call": round(vms * 1e3, 2),
+                                   "GBps": round(vbytes / (vms * 1e-3) / 1e9, 1),
+                                   "frac_hbm": round(vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "algorithmic_bytes_per_call": vbytes}
+        del vkv, vin, vws
+        torch.cuda.empty_cache()
 
     # ---------------- scaled caches: the 64K decode shape with INT8 and FP8 rows ----------------
     if not args.no_scaled:

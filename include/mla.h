@@ -98,19 +98,20 @@ extern "C" {
 #define MLA_MAX_HEADS 128   /* prefill: heads of one query token */
 
 /*
- * Workspace bytes for mla_decode and mla_prefill_varlen
+ * Workspace bytes for mla_decode, mla_decode_varlen and mla_prefill_varlen
  * [TALK, section "Kernel：让 MLA 真正跑满 GPU": the split parameters and the
  * workspace size are computed at run time and cached].
  *
- * One function serves both entry points.  For decode pass
- * max_q_len = q_len and total_q = batch * q_len; for prefill pass the
- * largest and the total number of new tokens.  The result is an upper bound
+ * One function serves every entry point.  For decode pass
+ * max_q_len = q_len and total_q = batch * q_len; for the other two pass the
+ * largest and the total number of query tokens.  The result is an upper bound
  * that depends only on these scalars and the current device's compute-unit
  * count, never on device-resident lengths, so a buffer sized once serves
  * every call with the same or smaller arguments.  It may be 0.
  *
- * Returns MLA_OK, MLA_ERR_INVALID (bytes_out NULL, a size < 1,
- * total_q < max_q_len), MLA_ERR_UNSUPPORTED (kv_dtype), or MLA_ERR_HIP when
+ * Returns MLA_OK, MLA_ERR_INVALID (bytes_out NULL, batch, num_heads or
+ * max_seq_len < 1, max_q_len or total_q < 0), MLA_ERR_UNSUPPORTED
+ * (kv_dtype), or MLA_ERR_HIP when
  * the device cannot be queried.
  */
 int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int total_q,
@@ -154,6 +155,35 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
                int batch, int q_len, int num_heads, int page_size, int max_seq_len,
                float softmax_scale, void* out, float* lse, void* workspace,
                size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Decode with a different number of query tokens per request: speculative
+ * decoding verifies a variable number of drafts per request [NEWS, section
+ * "TokenSpeed 性能預覽": speculative decoding, drafts causal among
+ * themselves].  Everything is as for mla_decode except the query layout:
+ *
+ *   q              bf16 [total_q, num_heads, 576], packed: request b's
+ *                  tokens are cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1
+ *   cu_seqlens_q   int32 [batch+1] on the device, cu_seqlens_q[0] = 0,
+ *                  nondecreasing, n_b = cu_seqlens_q[b+1] - cu_seqlens_q[b]
+ *                  <= max_q_len and n_b <= seq_lens[b] (preconditions)
+ *   total_q        cu_seqlens_q[batch] (host), 0 <= total_q <= batch * max_q_len
+ *   max_q_len      host upper bound of n_b; max_q_len * num_heads <= 128
+ *   out, lse       [total_q, num_heads, 512] bf16 and [total_q, num_heads] fp32
+ *   workspace      at least mla_splitkv_workspace_size(batch, num_heads,
+ *                  max_q_len, total_q, max_seq_len, kv_dtype) bytes
+ *
+ * Token i of request b (0-based) sees rows 0 .. seq_lens[b] - n_b + i.  A
+ * request with n_b = 0 produces nothing; total_q = 0 enqueues nothing (and
+ * then only the scalar arguments are checked: pointers may be NULL).
+ * Returns as mla_decode, plus MLA_ERR_INVALID for a null cu_seqlens_q or a
+ * total_q outside 0 .. batch * max_q_len.
+ */
+int mla_decode_varlen(const void* q, const int32_t* cu_seqlens_q, const void* kv_cache, const float* kv_scale,
+                      int kv_dtype, const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens,
+                      int batch, int total_q, int max_q_len, int num_heads, int page_size, int max_seq_len,
+                      float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* hip_stream);
 
 /*
  * Variable-length prefill after a cached prefix, without padding

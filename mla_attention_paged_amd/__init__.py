@@ -52,6 +52,9 @@ def library():
         lib.mla_decode.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp,
                                    vp, sz, vp]
         lib.mla_decode.restype = i32
+        lib.mla_decode_varlen.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
+                                          vp, vp, vp, sz, vp]
+        lib.mla_decode_varlen.restype = i32
         lib.mla_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
                                            f32, vp, vp, vp, sz, vp]
         lib.mla_prefill_varlen.restype = i32
@@ -115,6 +118,17 @@ def mla_decode(q, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, s
                               max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                               int(workspace_bytes), _stream(hip_stream))
     _check(rc, "mla_decode")
+
+
+def mla_decode_varlen(q, cu_seqlens_q, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, seq_lens,
+                      batch, total_q, max_q_len, num_heads, page_size, max_seq_len, softmax_scale, out, lse,
+                      workspace, workspace_bytes, hip_stream=None) -> None:
+    rc = library().mla_decode_varlen(_ptr(q), _ptr(cu_seqlens_q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype,
+                                     _ptr(page_table), max_pages_per_req, _ptr(seq_lens), batch, total_q,
+                                     max_q_len, num_heads, page_size, max_seq_len, float(softmax_scale),
+                                     _ptr(out), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                     _stream(hip_stream))
+    _check(rc, "mla_decode_varlen")
 
 
 def mla_prefill_varlen(q, cu_seqlens_q, prefix_lens, kv_cache, kv_scale, kv_dtype, page_table,

@@ -8,6 +8,7 @@
 // it per (device, shape) and is guarded by a mutex.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <map>
@@ -130,9 +131,10 @@ int cached_decode_plan(int batch, int heads, int q_len, int max_seq_len, int kv_
   return MLA_OK;
 }
 
+// Shapes a decode call (uniform or per-request query counts) can take.
 bool decode_shape(int batch, int num_heads, int max_q_len, int total_q) {
   return (long long)max_q_len * num_heads <= MLA_MAX_DECODE_ROWS &&
-         (long long)batch * max_q_len == total_q;
+         (long long)batch * max_q_len >= total_q;
 }
 
 bool known_dtype(int kv_dtype) {
@@ -176,8 +178,7 @@ int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int tota
                                int kv_dtype, size_t* bytes_out) {
   if (!bytes_out) return MLA_ERR_INVALID;
   *bytes_out = 0;
-  if (batch < 1 || num_heads < 1 || max_q_len < 0 || total_q < max_q_len || max_seq_len < 1)
-    return MLA_ERR_INVALID;
+  if (batch < 1 || num_heads < 1 || max_q_len < 0 || total_q < 0 || max_seq_len < 1) return MLA_ERR_INVALID;
   if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   int dev = 0, cus = 0;
   const int rc = device_cus(&dev, &cus);
@@ -197,14 +198,22 @@ int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int tota
   return MLA_OK;
 }
 
-int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
-               const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens, int batch,
-               int q_len, int num_heads, int page_size, int max_seq_len, float softmax_scale, void* out,
-               float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
-  // ---- host-scalar checks, before any HIP call ----
-  if (!q || !kv_cache || !page_table || !seq_lens || !out || !lse) return MLA_ERR_INVALID;
+}  // extern "C"
+
+namespace {
+
+// Decode with uniform (cu_q null: q_len tokens per request) or per-request
+// query counts (cu_q: device offsets, q_len the largest count, total_q the
+// total).  Host-scalar checks come first, before any HIP call.
+int decode_impl(const void* q, const int32_t* cu_q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens, int batch,
+                int total_q, int q_len, int num_heads, int page_size, int max_seq_len, float softmax_scale,
+                void* out, float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (batch < 1 || q_len < 1 || num_heads < 1 || max_pages_per_req < 1 || max_seq_len < 1)
     return MLA_ERR_INVALID;
+  if (total_q < 0 || (long long)total_q > (long long)batch * q_len) return MLA_ERR_INVALID;
+  // with no query token nothing is read or written: only the scalars are checked
+  if (total_q > 0 && (!q || !kv_cache || !page_table || !seq_lens || !out || !lse)) return MLA_ERR_INVALID;
   if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   if (kv_dtype != MLA_KV_BF16 && !kv_scale) return MLA_ERR_INVALID;
   if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
@@ -215,6 +224,8 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
   if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)batch * q_len * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_INVALID;
+
+  if (total_q == 0) return MLA_OK;  // no query rows: nothing to compute or write
 
   DecodePlan plan{};
   const int rc = cached_decode_plan(batch, num_heads, q_len, max_seq_len, kv_dtype, &plan);
@@ -228,6 +239,7 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
   a.kv_scale = kv_scale;
   a.page_table = page_table;
   a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
   a.max_pages = max_pages_per_req;
   a.batch = batch;
   a.q_len = q_len;
@@ -245,6 +257,31 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
   }
   const hipError_t e = launch_decode(plan, a, kv_dtype, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+               const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens, int batch,
+               int q_len, int num_heads, int page_size, int max_seq_len, float softmax_scale, void* out,
+               float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (batch < 1 || q_len < 1) return MLA_ERR_INVALID;
+  return decode_impl(q, nullptr, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, seq_lens, batch,
+                     (int)std::min<long long>((long long)batch * q_len, 0x7fffffffLL), q_len, num_heads,
+                     page_size, max_seq_len, softmax_scale, out, lse, workspace, workspace_bytes, hip_stream);
+}
+
+int mla_decode_varlen(const void* q, const int32_t* cu_seqlens_q, const void* kv_cache, const float* kv_scale,
+                      int kv_dtype, const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens,
+                      int batch, int total_q, int max_q_len, int num_heads, int page_size, int max_seq_len,
+                      float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  if (!cu_seqlens_q) return MLA_ERR_INVALID;
+  return decode_impl(q, cu_seqlens_q, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, seq_lens,
+                     batch, total_q, max_q_len, num_heads, page_size, max_seq_len, softmax_scale, out, lse,
+                     workspace, workspace_bytes, hip_stream);
 }
 
 int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t* prefix_lens,

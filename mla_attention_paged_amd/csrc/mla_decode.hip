@@ -53,12 +53,13 @@ __device__ __forceinline__ int owner_group(long long p, long long P, int G) {
 }
 
 // Write the rows of one finished (request, share) pair: the final output
-// when phase one is the only phase, else the partial in slot `slot`.  Wave
+// (rows of the request whose first query token is tok0) when phase one is
+// the only phase, else the partial in slot `slot`.  Wave
 // half h writes value columns 256h .. 256h + 255; half 0 writes the LSE.
 // Partial outputs are normalised (o / sum, a weighted mean of value rows)
 // and stored in bf16 like the final output, halving the workspace traffic;
 // their log2-sum-exp stays fp32.
-__device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& st, int b, int slot,
+__device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& st, int tok0, int slot,
                                            int row, bool row_ok, int half, int lane) {
   float inv, lse2;
   finish_row(st, inv, lse2);
@@ -66,7 +67,7 @@ __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& 
   const int g = lane >> 4;
   const int col0 = (kDv / 2) * half + 4 * g;
   const bool final_out = a.grid == 1;
-  uint16_t* dst = (final_out ? a.out + ((size_t)b * a.rows + row) * kDv
+  uint16_t* dst = (final_out ? a.out + ((size_t)tok0 * a.heads + row) * kDv
                              : a.part_o + ((size_t)slot * a.rows + row) * kDv) + col0;
 #pragma unroll
   for (int ct = 0; ct < kOHalf; ++ct) {
@@ -77,7 +78,7 @@ __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& 
   }
   if (g == 0 && half == 0) {
     if (final_out)
-      a.lse[(size_t)b * a.rows + row] = lse2 * kLn2;
+      a.lse[(size_t)tok0 * a.heads + row] = lse2 * kLn2;
     else
       a.part_lse[(size_t)slot * a.rows + row] = lse2;
   }
@@ -96,11 +97,28 @@ struct Lens {
   }
 };
 
+// Query tokens of request b: its first token and its count (uniform q_len,
+// or the per-request offsets, cached in LDS like the lengths).
+struct ReqQ {
+  int tok0, n;
+};
+
+__device__ __forceinline__ ReqQ req_q(const DecodeArgs& a, const int* s_tok, int b) {
+  if (!a.cu_q) return {b * a.q_len, a.q_len};
+  if (b < kLenCache) return {s_tok[b], s_tok[b + 1] - s_tok[b]};
+  const int t0 = a.cu_q[b];
+  return {t0, a.cu_q[b + 1] - t0};
+}
+
 // Wave 0 of workgroup g locates its share floor(g*P/G) .. floor((g+1)*P/G)
 // of the page stream and the (request, page) where it starts, and fills the
-// length cache; workgroup (0, 0) also records the page prefix sums for the
-// merge.
-__device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lane, int* s_info, int* s_len) {
+// length cache (and, for per-request query counts, the token-offset cache,
+// entries 0 .. min(batch, kLenCache)); workgroup (0, 0) also records the
+// page prefix sums for the merge.
+__device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lane, int* s_info, int* s_len,
+                                             int* s_tok) {
+  if (a.cu_q)
+    for (int b = lane; b <= a.batch && b <= kLenCache; b += 64) s_tok[b] = a.cu_q[b];
   const int G = a.grid;
   long long P = 0;
   const bool write_cum = g == 0 && blockIdx.y == 0 && G > 1;
@@ -215,11 +233,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   __shared__ int s_pid[2 * kWin], s_req[2 * kWin], s_rem[2 * kWin];
   __shared__ int s_info[5];
   __shared__ int s_len[kLenCache];
+  __shared__ int s_tok[kLenCache + 1];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = blockIdx.x;
-  if (w == 0) locate_share(a, g, lane, s_info, s_len);
+  if (w == 0) locate_share(a, g, lane, s_info, s_len, s_tok);
   __syncthreads();
   const Lens lens{a, s_len};
   const int seg_lo = s_info[0], seg_hi = s_info[1];
@@ -229,9 +248,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   const int half = w >> 2;
   const int row = kBlockRows * blockIdx.y + 16 * (w & 3) + (lane & 15);
   const bool wave_rows = kBlockRows * blockIdx.y + 16 * (w & 3) < a.rows;
-  const bool row_ok = row < a.rows;
-  const int draft = row_ok ? row / a.heads : 0;
-  const int late = a.q_len - draft;  // row sees rows t <= L - late
+  // the current request's query rows: this lane's row exists when
+  // row < n * heads, and its token (row / heads) sees rows t <= L - late
+  bool row_ok = false;
+  int late = 0, tok0 = 0;
+  auto set_req = [&](int b) {
+    const ReqQ r = req_q(a, s_tok, b);
+    row_ok = row < r.n * a.heads;
+    late = r.n - (row_ok ? row / a.heads : 0);
+    tok0 = r.tok0;
+  };
   MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
   MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
   auto stage = [&](int t) { return ring + (t % kPStages) * kStageBytes; };
@@ -243,7 +269,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   // fill and the first tile; the first tile's wait covers them.
   int q_b = -1;  // request whose query fragments are loaded or in flight
   if (wave_rows && cb < a.batch) {
-    issue_q(row_ok ? a.q + ((size_t)cb * a.rows + row) * kDqk : nullptr, lane, qf);
+    set_req(cb);
+    issue_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
     q_b = cb;
   }
 
@@ -263,8 +290,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
       int t1 = t0 + 1;
       while (t1 < N && (s_req[t1] >> 1) == b) ++t1;
       if (wave_rows && b != cur_b) {
-        if (cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
-        if (b != q_b) load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+        if (cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
+        set_req(b);
+        if (b != q_b) load_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
         q_b = -1;
         reset_state(st);
       }
@@ -307,7 +335,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
       t0 = t1;
     }
   }
-  if (wave_rows && cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
+  if (wave_rows && cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
 }
 
 // Phase one for an INT8 or FP8 cache (CODE), software-pipelined like the
@@ -335,11 +363,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs
   __shared__ int s_pid[2 * kWin], s_req[2 * kWin], s_rem[2 * kWin];
   __shared__ int s_info[5];
   __shared__ int s_len[kLenCache];
+  __shared__ int s_tok[kLenCache + 1];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = blockIdx.x;
-  if (w == 0) locate_share(a, g, lane, s_info, s_len);
+  if (w == 0) locate_share(a, g, lane, s_info, s_len, s_tok);
   __syncthreads();
   const Lens lens{a, s_len};
   const int seg_lo = s_info[0], seg_hi = s_info[1];
@@ -349,9 +378,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs
   const int half = w >> 2;
   const int row = kBlockRows * blockIdx.y + 16 * (w & 3) + (lane & 15);
   const bool wave_rows = kBlockRows * blockIdx.y + 16 * (w & 3) < a.rows;
-  const bool row_ok = row < a.rows;
-  const int draft = row_ok ? row / a.heads : 0;
-  const int late = a.q_len - draft;  // row sees rows t <= L - late
+  // the current request's query rows: this lane's row exists when
+  // row < n * heads, and its token (row / heads) sees rows t <= L - late
+  bool row_ok = false;
+  int late = 0, tok0 = 0;
+  auto set_req = [&](int b) {
+    const ReqQ r = req_q(a, s_tok, b);
+    row_ok = row < r.n * a.heads;
+    late = r.n - (row_ok ? row / a.heads : 0);
+    tok0 = r.tok0;
+  };
   MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
   MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
   auto code_stage = [&](int t) { return codes + (t % kCStages) * kI8StageBytes; };
@@ -363,7 +399,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs
   int cur_b = -1;
   int q_b = -1;  // request whose query fragments are loaded or in flight
   if (wave_rows && cb < a.batch) {
-    issue_q(row_ok ? a.q + ((size_t)cb * a.rows + row) * kDqk : nullptr, lane, qf);
+    set_req(cb);
+    issue_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
     q_b = cb;
   }
 
@@ -399,8 +436,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs
       int t1 = t0 + 1;
       while (t1 < N && (s_req[t1] >> 1) == b) ++t1;
       if (wave_rows && b != cur_b) {
-        if (cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
-        if (b != q_b) load_q(row_ok ? a.q + ((size_t)b * a.rows + row) * kDqk : nullptr, lane, qf);
+        if (cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
+        set_req(b);
+        if (b != q_b) load_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
         q_b = -1;
         reset_state(st);
       }
@@ -440,7 +478,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs
       t0 = t1;
     }
   }
-  if (wave_rows && cur_b >= 0) flush_rows(a, st, cur_b, g + cur_b, row, row_ok, half, lane);
+  if (wave_rows && cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
 }
 
 // Phase two: per (request, row), reduce the partials of the workgroups
@@ -471,6 +509,12 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int R = blockIdx.x;
   const int quarter = blockIdx.y;
   const int b = R / a.rows, row = R - b * a.rows;
+  int tok0 = b * a.q_len;
+  if (a.cu_q) {
+    tok0 = a.cu_q[b];
+    if (row >= (a.cu_q[b + 1] - tok0) * a.heads) return;  // a row the request does not have
+  }
+  const size_t orow = (size_t)tok0 * a.heads + row;     // output row
   const long long P = a.cum_pages[a.batch];
   const int G = a.grid;
   const long long p0 = a.cum_pages[b], p1 = a.cum_pages[b + 1];
@@ -536,8 +580,8 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
     bf16x4 h;
     h[0] = (__bf16)(o[0] * inv); h[1] = (__bf16)(o[1] * inv);
     h[2] = (__bf16)(o[2] * inv); h[3] = (__bf16)(o[3] * inv);
-    *reinterpret_cast<bf16x4*>(a.out + (size_t)R * kDv + col) = h;
-    if (quarter == 0 && tid == 0) a.lse[R] = tot > 0.f ? (m_use + fast_log2(tot)) * kLn2 : -INFINITY;
+    *reinterpret_cast<bf16x4*>(a.out + orow * kDv + col) = h;
+    if (quarter == 0 && tid == 0) a.lse[orow] = tot > 0.f ? (m_use + fast_log2(tot)) * kLn2 : -INFINITY;
   }
 }
 

@@ -20,11 +20,12 @@ struct DecodeArgs {
   const float* kv_scale;      // int8 only
   const int32_t* page_table;  // [batch, max_pages]
   const int32_t* seq_lens;    // [batch]
+  const int32_t* cu_q;        // [batch + 1] first query token of each request, or null: b * q_len
   int max_pages;
   int batch;
-  int q_len;
+  int q_len;                  // query tokens per request (with cu_q: the largest)
   int heads;
-  int rows;                   // q_len * heads: folded query rows of one request
+  int rows;                   // q_len * heads: folded query rows of one request (with cu_q: at most)
   int grid;                   // phase-one workgroups
   float scale_log2;           // softmax_scale * log2(e)
   uint16_t* out;              // bf16 [batch * rows, 512]

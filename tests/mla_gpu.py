@@ -87,3 +87,20 @@ def assert_close(out, lse, ref_out, ref_lse, what=""):
     # diagnostic: relative Frobenius error per (token, head) row
     rel = np.linalg.norm(out - ref_out, axis=-1) / np.maximum(np.linalg.norm(ref_out, axis=-1), 1e-30)
     return float(err.max()), float(lerr.max()), float(rel.max())
+
+
+def run_decode_varlen(case, inputs=None, max_q_len=None, stream=None):
+    """mla_decode_varlen on a PrefillCase read as a ragged decode (request b's n_b query
+    tokens are the last n_b of its seq_lens[b] cached rows)."""
+    d = inputs or prefill_inputs(case)
+    T, H = case.total_q(), case.heads
+    mq = max_q_len or max(1, case.max_q_len())
+    out = torch.empty((max(T, 1), H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((max(T, 1), H), dtype=torch.float32, device="cuda")
+    lens = torch.from_numpy(case.cache.kv_lens.copy()).cuda()
+    nbytes = mla.mla_splitkv_workspace_size(case.batch, H, mq, T, case.max_seq_len, d["kind"])
+    workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    mla.mla_decode_varlen(d["q"], d["cu"], d["kv"], d["scale"], d["kind"], d["pt"], case.cache.max_pages, lens,
+                          case.batch, T, mq, H, 64, case.max_seq_len, case.softmax_scale, out, lse, workspace,
+                          workspace.numel(), stream)
+    return out, lse

@@ -124,7 +124,8 @@ def test_workspace_size_argument_checks(lib):
     out = ctypes.c_size_t(0)
     assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 0, None) == mla.MLA_ERR_INVALID
     assert lib.mla_splitkv_workspace_size(0, 16, 4, 16, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
-    assert lib.mla_splitkv_workspace_size(4, 16, 4, 3, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
+    assert lib.mla_splitkv_workspace_size(4, 16, 4, -1, 1024, 0, ctypes.byref(out)) == mla.MLA_ERR_INVALID
+    assert lib.mla_splitkv_workspace_size(4, 16, 4, 3, 1024, 0, ctypes.byref(out)) == mla.MLA_OK  # ragged decode
     assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 7, ctypes.byref(out)) == mla.MLA_ERR_UNSUPPORTED
     assert lib.mla_splitkv_workspace_size(4, 16, 4, 16, 1024, 2, ctypes.byref(out)) == mla.MLA_OK
 
@@ -154,3 +155,35 @@ def _append_rc(lib, **kw):
 ])
 def test_append_argument_checks(lib, kw, code):
     assert _append_rc(lib, **kw) == code
+
+
+def _varlen_rc(lib, **kw):
+    a = dict(q=1, cu=1, kv=1, scale=None, kind=0, pt=1, maxp=1024, lens=1, batch=4, tq=10, mq=4, heads=16,
+             page=64, maxlen=65536, sf=0.07, out=1, lse=1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.mla_decode_varlen(a["q"], a["cu"], a["kv"], a["scale"], a["kind"], a["pt"], a["maxp"], a["lens"],
+                                 a["batch"], a["tq"], a["mq"], a["heads"], a["page"], a["maxlen"], a["sf"],
+                                 a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), mla.MLA_ERR_INVALID),
+    (dict(q=None), mla.MLA_ERR_INVALID),
+    (dict(tq=17), mla.MLA_ERR_INVALID),             # more tokens than batch * max_q_len
+    (dict(tq=-1), mla.MLA_ERR_INVALID),
+    (dict(mq=0), mla.MLA_ERR_INVALID),
+    (dict(mq=9), mla.MLA_ERR_UNSUPPORTED),          # 144 folded rows
+    (dict(kind=2), mla.MLA_ERR_INVALID),            # fp8 without scales
+    (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(maxlen=3), mla.MLA_ERR_INVALID),
+    (dict(ws=None, wsb=0), mla.MLA_ERR_WORKSPACE),
+    (dict(tq=0), mla.MLA_OK),                       # nothing to do, no launch
+])
+def test_decode_varlen_argument_checks(lib, kw, code):
+    assert _varlen_rc(lib, **kw) == code
+
+
+def test_workspace_covers_varlen_decode(lib):
+    # fewer tokens than batch * max_q_len still sizes the decode split
+    ws = mla.mla_splitkv_workspace_size(4, 16, 4, 10, 65536, 0)
+    assert ws >= mla.mla_decode_plan(4, 16, 4, 65536, 0, num_cus=256)[1]
