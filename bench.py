@@ -60,7 +60,7 @@ def decode_algorithmic_bytes(case) -> int:
     L = c.kv_lens.astype(np.int64)
     row_bytes = 576 * 2 if c.kv_dtype == "bf16" else 576 + 4
     T, H = case.total_q(), case.heads
-    pages = int(((L + 63) // 64).sum())
+    pages = int(((L + c.page_size - 1) // c.page_size).sum())  # page-table entries read
     return int(L.sum() * row_bytes + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4 + pages * 4
                + case.batch * 4)
 
@@ -197,11 +197,13 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-pages", action="store_true",
+                    help="skip the page-size leg (the 64K decode with 128- and 1536-row pages)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the ragged-draft decode leg (1..4 drafts per request) on the 64K decode shape")
     ap.add_argument("--no-scaled", action="store_true",
@@ -319,6 +321,31 @@ def main() -> int:
                          "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
         }
 
+    # ---------------- page sizes: the 64K decode with 128- and 1536-row pages ----------------
+    if not args.no_pages:
+        legs = {}
+        for ps in (128, 1536):
+            pcase2 = synth.make_decode_case(2, case.batch, H, case.q_len, seq_lens=case.seq_lens.tolist(), page_size=ps)
+            pin2 = decode_inputs(pcase2)
+            pkv = [pin2["kv"]] + [pin2["kv"].clone() for _ in range(max(0, args.copies - 1))]
+
+            def make_pcall(kv, pin2=pin2, pcase2=pcase2, ps=ps):
+                def call():
+                    mla.mla_decode(pin2["q"], kv, None, 0, pin2["pt"], pcase2.cache.max_pages, pin2["seq_lens"],
+                                   pcase2.batch, pcase2.q_len, H, ps, pcase2.max_seq_len, pcase2.softmax_scale,
+                                   out, lse, ws, ws.numel(), stream)
+                return call
+
+            psteps = max(20, args.steps // 2)
+            pms = time_calls([make_pcall(kv) for kv in pkv], stream, args.warmup, psteps) / psteps
+            pbytes = decode_algorithmic_bytes(pcase2)
+            legs[str(ps)] = {"us_per_call": round(pms * 1e3, 2),
+                             "GBps": round(pbytes / (pms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del pkv, pin2
+            torch.cuda.empty_cache()
+        result["page_sizes"] = {"workload": f"{case.name} with pages of 128 and 1536 rows", **legs}
+
     # ---------------- ragged drafts: the 64K decode shape with 1, 2, 3, 4 drafts ----------------
     if not args.no_varlen:
         qls = np.array([1, 2, 3, 4], np.int32)
@@ -340,7 +367,7 @@ def main() -> int:
             return call
 
         vsteps = max(20, args.steps // 2)
-        vms = time_calls([make_vcall(kv) for kv in vkv], stream, max(10, args.warmup // 2), vsteps) / vsteps
+        vms = time_calls([make_vcall(kv) for kv in vkv], stream, args.warmup, vsteps) / vsteps
         L = vcase.cache.kv_lens.astype(np.int64)
         vbytes = int(L.sum() * 1152 + vT * H * (576 * 2 + 512 * 2 + 4) + int(((L + 63) // 64).sum()) * 4
                      + vcase.batch * 8)
@@ -371,7 +398,7 @@ def main() -> int:
                 return call
 
             ssteps = max(20, args.steps // 2)
-            sms = time_calls([make_scall(kv) for kv in skv], stream, max(10, args.warmup // 2), ssteps) / ssteps
+            sms = time_calls([make_scall(kv) for kv in skv], stream, args.warmup, ssteps) / ssteps
             sbytes = decode_algorithmic_bytes(scase)
             gbs = sbytes / (sms * 1e-3) / 1e9
             legs[dt] = {"us_per_call": round(sms * 1e3, 2), "GBps": round(gbs, 1),
@@ -410,7 +437,8 @@ def main() -> int:
                 mla.mla_kv_append(new, cu, start, kv, sc, kind, pt_d, pt.shape[1], acase.batch, rows, 64, stream)
 
             asteps = 200
-            ams = time_calls([acall], stream, 20, asteps) / asteps
+            # ~20 ms of warm-up calls: the clocks ramp up again after the idle input generation
+            ams = time_calls([acall], stream, 4000, asteps) / asteps
             abytes = rows * (1152 + row_out)  # rows read + rows (and scales) written
             legs[name] = {"us_per_call": round(ams * 1e3, 2), "GBps": round(abytes / (ams * 1e-3) / 1e9, 1),
                           "frac_hbm": round(abytes / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -31,11 +31,16 @@
  *
  * Memory layouts (all device memory, all row-major, no padding):
  *   query      bf16 [tokens, num_heads, 576]
- *   kv_cache   bf16, int8 or fp8 [num_pages, page_size, 576]; page_size must
- *              be 64
+ *   kv_cache   bf16, int8 or fp8 [num_pages, page_size, 576]; page_size is
+ *              a multiple of 64 up to MLA_MAX_PAGE_SIZE
  *   kv_scale   fp32 [num_pages, page_size]: per-row scale of the int8 and
  *              fp8 caches (row value = code * scale, or e4m3(code) * scale);
  *              NULL for a bf16 cache
+ *   page_table int32 [batch, max_pages_per_req]: physical page of logical
+ *              page j of request b (rows j * page_size ..); only entries
+ *              j < ceil(L_b / page_size) are read
+ *   out        bf16 [tokens, num_heads, 512]
+ *   lse        fp32 [tokens, num_heads]
  *
  * FP8 cache [GITREAD] "TokenSpeed 深度解析:把 LLM 推理压到"光速"意味着什么",
  * section "核心技术揭秘" (FP8 KV-cache quantisation, no format given): codes
@@ -44,10 +49,15 @@
  * magnitude 0x7F (NaN) must not occur in a cache.  Codes are widened to
  * bf16 exactly; attention then runs as for bf16 with the row scales applied
  * to the scores and probabilities.
- *   page_table int32 [batch, max_pages_per_req]: physical page of logical
- *              page j of request b; only entries j < ceil(L_b / 64) are read
- *   out        bf16 [tokens, num_heads, 512]
- *   lse        fp32 [tokens, num_heads]
+ *
+ * Page sizes [TALK, section "Runtime：构建可扩展的推理引擎架构": the engine's
+ * first cache managed blocks of 1536 tokens; its later two-level design has
+ * logical blocks of 128 tokens, for finer prefix reuse, inside physical
+ * blocks of 1536].  A page of page_size rows is, in memory, page_size / 64
+ * consecutive 64-row sub-pages, which is how the kernels walk it.  The
+ * two-level layout is page_size = 128 with each entry naming the 128-row
+ * block (physical block * 12 + slot) that holds the logical block; one-level
+ * 1536-row blocks are page_size = 1536.
  *
  * Ownership and streams.  The caller allocates every buffer; the library
  * never allocates or frees device memory, never synchronises, keeps no
@@ -62,7 +72,7 @@
  * preconditions, not checked: q_len <= seq_lens[b] <= max_seq_len (decode),
  * new tokens + prefix_lens[b] <= max_seq_len (prefill), and the page-table
  * entries that are read name pages that exist.  Lengths above
- * max_pages_per_req * 64 are clamped on the device so that the page table is
+ * max_pages_per_req * page_size are clamped on the device so that the page table is
  * never read out of bounds.
  *
  * Determinism.  For fixed inputs and shapes the results are bitwise
@@ -93,7 +103,8 @@ extern "C" {
 
 #define MLA_DIM_QK 576      /* cache row / query row width: 512 latent + 64 rope */
 #define MLA_DIM_V 512       /* value width: the first 512 columns of a row */
-#define MLA_PAGE_SIZE 64    /* the one supported page size */
+#define MLA_PAGE_SIZE 64    /* the kernels' sub-page: page sizes are multiples of it */
+#define MLA_MAX_PAGE_SIZE 4096 /* largest page size */
 #define MLA_MAX_DECODE_ROWS 128 /* q_len * num_heads of one decode request */
 #define MLA_MAX_HEADS 128   /* prefill: heads of one query token */
 
@@ -136,7 +147,7 @@ int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int tota
  *   seq_lens   int32 [batch] on the device: cached rows of request b,
  *              the q_len new tokens included
  *   max_seq_len  host upper bound of seq_lens; max_pages_per_req must be
- *              at least ceil(max_seq_len / 64)
+ *              at least ceil(max_seq_len / page_size)
  *   softmax_scale  multiplies <q, row> (for example 1/sqrt(192))
  *   out, lse   outputs, [batch * q_len, num_heads, 512] bf16 and
  *              [batch * q_len, num_heads] fp32
@@ -146,7 +157,8 @@ int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int tota
  *
  * Returns MLA_OK; MLA_ERR_INVALID for a null pointer, a size < 1, a
  * non-finite or non-positive softmax_scale, max_seq_len < q_len or
- * max_pages_per_req too small; MLA_ERR_UNSUPPORTED for page_size != 64,
+ * max_pages_per_req too small; MLA_ERR_UNSUPPORTED for a page_size that is
+ * not a multiple of 64 in 64 .. MLA_MAX_PAGE_SIZE,
  * q_len * num_heads > 128 or an unknown kv_dtype; MLA_ERR_WORKSPACE;
  * MLA_ERR_HIP.
  */
@@ -229,14 +241,15 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
  * decode stays bandwidth-bound even with an INT8 latent cache].  For request
  * b, new row j (0 <= j < n_b = cu_seqlens_new[b+1] - cu_seqlens_new[b]) is
  * row cu_seqlens_new[b] + j of kv_new and goes to logical position
- * t = start_pos[b] + j of the request: page page_table[b][t / 64], slot t % 64.
+ * t = start_pos[b] + j of the request: page page_table[b][t / page_size],
+ * slot t % page_size.
  *
  *   bf16 cache (kv_dtype 0): the 576 values are copied unchanged.
  *   int8 cache (kv_dtype 1): symmetric per-row quantisation with an fp32
  *     scale: scale = max_c |x_c| / 127 (fp32 division, rounded to nearest;
  *     an all-zero row gets scale 1), code_c = clamp(rint(x_c / scale),
  *     -127, 127) with ties to even; the codes go to the row of the int8 cache
- *     and the scale to kv_scale[page * 64 + slot].  Dequantised value:
+ *     and the scale to kv_scale[page * page_size + slot].  Dequantised value:
  *     code * scale, as the attention entry points read it.
  *   fp8 cache (kv_dtype 2) [GITREAD, section "核心技术揭秘"]: the same with
  *     scale = max_c |x_c| / 448 and code_c = the E4M3 value nearest to
@@ -249,15 +262,15 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
  *                   cu_seqlens_new[batch] = total_new
  *   start_pos       int32 [batch]: logical position of each request's first
  *                   new row (its cached length before the append)
- *   kv_cache        bf16, int8 or fp8 [num_pages, 64, 576], written in place
- *   kv_scale        fp32 [num_pages, 64] for an int8 or fp8 cache (written),
+ *   kv_cache        bf16, int8 or fp8 [num_pages, page_size, 576], written in place
+ *   kv_scale        fp32 [num_pages, page_size] for an int8 or fp8 cache (written),
  *                   else NULL
  *   page_table      int32 [batch, max_pages_per_req]
  *
- * Rows whose position falls outside 0 .. max_pages_per_req * 64 - 1 are not
+ * Rows whose position falls outside 0 .. max_pages_per_req * page_size - 1 are not
  * written.  Nothing else of the cache is touched.  The page-table entries of
  * the written positions must name existing pages (a precondition, as for the
- * attention entry points).  Returns MLA_ERR_UNSUPPORTED for page_size != 64
+ * attention entry points).  Returns MLA_ERR_UNSUPPORTED for an unsupported page_size
  * or an unknown kv_dtype, MLA_ERR_INVALID for null pointers (when
  * total_new > 0), batch < 1, total_new < 0, max_pages_per_req < 1 or an
  * int8 or fp8 cache without kv_scale.  total_new == 0 enqueues nothing.

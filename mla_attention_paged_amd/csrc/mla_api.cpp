@@ -137,6 +137,12 @@ bool decode_shape(int batch, int num_heads, int max_q_len, int total_q) {
          (long long)batch * max_q_len >= total_q;
 }
 
+// Page sizes: whole numbers of 64-row sub-pages (the kernels' unit), up to
+// MLA_MAX_PAGE_SIZE rows.
+bool known_page_size(int page_size) {
+  return page_size >= MLA_PAGE_SIZE && page_size <= MLA_MAX_PAGE_SIZE && page_size % MLA_PAGE_SIZE == 0;
+}
+
 bool known_dtype(int kv_dtype) {
   return kv_dtype == MLA_KV_BF16 || kv_dtype == MLA_KV_INT8 || kv_dtype == MLA_KV_FP8;
 }
@@ -216,11 +222,12 @@ int decode_impl(const void* q, const int32_t* cu_q, const void* kv_cache, const 
   if (total_q > 0 && (!q || !kv_cache || !page_table || !seq_lens || !out || !lse)) return MLA_ERR_INVALID;
   if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   if (kv_dtype != MLA_KV_BF16 && !kv_scale) return MLA_ERR_INVALID;
-  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (!known_page_size(page_size)) return MLA_ERR_UNSUPPORTED;
   if ((long long)q_len * num_heads > MLA_MAX_DECODE_ROWS) return MLA_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID;
   if (max_seq_len < q_len) return MLA_ERR_INVALID;
-  if ((long long)max_pages_per_req * MLA_PAGE_SIZE < max_seq_len) return MLA_ERR_INVALID;
+  if ((long long)max_pages_per_req * page_size < max_seq_len) return MLA_ERR_INVALID;
+  if ((long long)max_pages_per_req * page_size > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)batch * q_len * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_INVALID;
@@ -240,7 +247,9 @@ int decode_impl(const void* q, const int32_t* cu_q, const void* kv_cache, const 
   a.page_table = page_table;
   a.seq_lens = seq_lens;
   a.cu_q = cu_q;
-  a.max_pages = max_pages_per_req;
+  a.pt_stride = max_pages_per_req;
+  a.sub = page_size / MLA_PAGE_SIZE;
+  a.max_pages = max_pages_per_req * a.sub;
   a.batch = batch;
   a.q_len = q_len;
   a.heads = num_heads;
@@ -297,10 +306,11 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
   if (total_q < max_q_len || max_seq_len < max_q_len) return MLA_ERR_INVALID;
   if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   if (kv_dtype != MLA_KV_BF16 && !kv_scale) return MLA_ERR_INVALID;
-  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (!known_page_size(page_size)) return MLA_ERR_UNSUPPORTED;
   if (num_heads > MLA_MAX_HEADS) return MLA_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID;
-  if ((long long)max_pages_per_req * MLA_PAGE_SIZE < max_seq_len) return MLA_ERR_INVALID;
+  if ((long long)max_pages_per_req * page_size < max_seq_len) return MLA_ERR_INVALID;
+  if ((long long)max_pages_per_req * page_size > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if ((long long)total_q * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_INVALID;
@@ -319,7 +329,9 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
   a.kv = static_cast<const uint8_t*>(kv_cache);
   a.kv_scale = kv_scale;
   a.page_table = page_table;
-  a.max_pages = max_pages_per_req;
+  a.pt_stride = max_pages_per_req;
+  a.sub = page_size / MLA_PAGE_SIZE;
+  a.max_pages = max_pages_per_req * a.sub;
   a.batch = batch;
   a.total_q = total_q;
   a.heads = num_heads;
@@ -341,12 +353,12 @@ int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32
                   int max_pages_per_req, int batch, int total_new, int page_size, void* hip_stream) {
   if (batch < 1 || total_new < 0 || max_pages_per_req < 1) return MLA_ERR_INVALID;
   if (!known_dtype(kv_dtype)) return MLA_ERR_UNSUPPORTED;
-  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (!known_page_size(page_size)) return MLA_ERR_UNSUPPORTED;
   if (total_new > 0 && (!kv_new || !cu_seqlens_new || !start_pos || !kv_cache || !page_table))
     return MLA_ERR_INVALID;
   if (kv_dtype != MLA_KV_BF16 && !kv_scale) return MLA_ERR_INVALID;
   if ((long long)batch * max_pages_per_req > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
-  if ((long long)max_pages_per_req * MLA_PAGE_SIZE > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if ((long long)max_pages_per_req * page_size > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if (total_new == 0) return MLA_OK;
 
   AppendArgs a{};
@@ -357,7 +369,9 @@ int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32
   a.kv_scale = kv_dtype != MLA_KV_BF16 ? kv_scale : nullptr;  // the kernel keys on it
   a.code = kv_dtype;
   a.page_table = page_table;
-  a.max_pages = max_pages_per_req;
+  a.pt_stride = max_pages_per_req;
+  a.sub = page_size / MLA_PAGE_SIZE;
+  a.max_pages = max_pages_per_req * a.sub;
   a.batch = batch;
   a.total_new = total_new;
   const hipError_t e = launch_append(a, kv_dtype, static_cast<hipStream_t>(hip_stream));

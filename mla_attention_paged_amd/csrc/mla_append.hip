@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void kv_append(AppendArgs a) {
   const int b = lo;
   const int t = a.start_pos[b] + (r - a.cu[b]);
   if (t < 0 || t >= a.max_pages * kPage) return;  // outside the request's page table
-  const size_t pos = (size_t)a.page_table[(size_t)b * a.max_pages + (t >> 6)] * kPage + (t & (kPage - 1));
+  const size_t pos = (size_t)sub_page(a.page_table, (size_t)b * a.pt_stride, t >> 6, a.sub) * kPage + (t & (kPage - 1));
   const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv_new + (size_t)r * kDqk);
   const bool two = lane < kRowChunks - 64;  // lanes holding a second chunk
 

@@ -189,7 +189,7 @@ __device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, const Len
       const int incl = wave_incl_scan(nt, lane);
       if (k < n) {
         const int t = base + incl - nt;
-        const int pid = a.page_table[(size_t)b * a.max_pages + off];
+        const int pid = sub_page(a.page_table, (size_t)b * a.pt_stride, off, a.sub);
         const int rem = Lc - kPage * off;
         s_pid[t] = pid;
         s_req[t] = 2 * b;

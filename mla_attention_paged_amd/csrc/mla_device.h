@@ -91,6 +91,16 @@ constexpr int kWaves = 8;                      // waves per workgroup (two per S
 constexpr int kBlockRows = 64;                 // query rows per workgroup
 constexpr int kOHalf = kOFrags / 2;            // value-column tiles per wave
 
+// Pages of sub * 64 rows are laid out as sub consecutive 64-row sub-pages,
+// so the kernels walk the cache in 64-row sub-pages: logical sub-page j of
+// the request whose page-table row starts at `row` is sub-page
+// (entry j / sub) * sub + j % sub of the cache.
+__device__ __forceinline__ int sub_page(const int32_t* __restrict__ page_table, size_t row, int j, int sub) {
+  if (sub == 1) return page_table[row + j];
+  const int e = j / sub;
+  return page_table[row + e] * sub + (j - e * sub);
+}
+
 // Byte offset of 16-byte chunk `chunk` of token `t` inside a staged page.
 __device__ __forceinline__ int tile_off(int t, int chunk) { return t * kLdsPitch + chunk * 16; }
 

@@ -21,7 +21,9 @@ struct DecodeArgs {
   const int32_t* page_table;  // [batch, max_pages]
   const int32_t* seq_lens;    // [batch]
   const int32_t* cu_q;        // [batch + 1] first query token of each request, or null: b * q_len
-  int max_pages;
+  int max_pages;              // 64-row sub-pages a request can hold (page-table entries * sub)
+  int pt_stride;              // page-table entries per request
+  int sub;                    // 64-row sub-pages per page (page size / 64)
   int batch;
   int q_len;                  // query tokens per request (with cu_q: the largest)
   int heads;
@@ -43,7 +45,9 @@ struct PrefillArgs {
   const uint8_t* kv;
   const float* kv_scale;
   const int32_t* page_table;
-  int max_pages;
+  int max_pages;              // 64-row sub-pages a request can hold (page-table entries * sub)
+  int pt_stride;              // page-table entries per request
+  int sub;                    // 64-row sub-pages per page (page size / 64)
   int batch;
   int total_q;
   int heads;
@@ -63,8 +67,10 @@ struct AppendArgs {
   const int32_t* start_pos;   // [batch] logical position of each request's first new row
   uint8_t* kv;                // pages, bf16 or int8 rows, written in place
   float* kv_scale;            // int8 only: [num_pages, 64]
-  const int32_t* page_table;  // [batch, max_pages]
-  int max_pages;
+  const int32_t* page_table;  // [batch, pt_stride]
+  int max_pages;              // 64-row sub-pages a request can hold (page-table entries * sub)
+  int pt_stride;              // page-table entries per request
+  int sub;                    // 64-row sub-pages per page (page size / 64)
   int batch;
   int total_new;
   int code;                   // scaled caches: 1 INT8, 2 FP8 (E4M3)

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_codes(Prefi
       const int n = min(kPWin, wt.npages - plo);
       __syncthreads();
       for (int k = threadIdx.x; k < n; k += kWaves * 64)
-        s_pid[k] = a.page_table[(size_t)wt.b * a.max_pages + plo + k];
+        s_pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
       __syncthreads();
       // tiles of 32 rows: only those holding a row the tile's last token sees
       const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_bf16(Prefil
       const int n = min(kPWin, wt.npages - plo);
       __syncthreads();  // the previous window's list and stages are no longer read
       for (int k = threadIdx.x; k < n; k += kWaves * 64)
-        s_pid[k] = a.page_table[(size_t)wt.b * a.max_pages + plo + k];
+        s_pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
       __syncthreads();
       const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
       auto issue = [&](int k) {

@@ -7,8 +7,9 @@ What it follows.  [TALK] "æž„å»ºé¢å‘ Agentic æŽ¨ç†çš„ä¸‹ä¸€ä»£ LLM æŽ¨ç†å¼•æ
 "Kernelï¼šè®© MLA çœŸæ­£è·‘æ»¡ GPU": attention runs over a paged cache of compressed
 latent rows, one row per token, and an INT8 latent cache is one way to cut the
 bandwidth decode needs.  The cache layout and the INT8 encoding are the ones
-the attention entry points read: page ``page_table[b][t // 64]``, slot
-``t % 64`` for logical position ``t`` of request ``b``; an INT8 row is
+the attention entry points read: page ``page_table[b][t // page_size]``, slot
+``t % page_size`` for logical position ``t`` of request ``b`` (the page size is
+the cache's second dimension); an INT8 row is
 576 codes plus one fp32 scale, value = code * scale, symmetric, per row.
 
 The quantisation is written out as its definition, in fp32 as the cache stores
@@ -94,9 +95,9 @@ def kv_append(kv_new_bits: np.ndarray, cu_seqlens_new: np.ndarray, start_pos: np
               quantize_fp8=quantize_row_fp8) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Return copies of ``cache`` (and ``kv_scale``) with the new rows written.
 
-    kv_new_bits: uint16 bf16 bits [total_new, 576]; cache: [num_pages, 64, 576]
+    kv_new_bits: uint16 bf16 bits [total_new, 576]; cache: [num_pages, page_size, 576]
     (uint16 bf16 bits, or int8 / uint8 E4M3 codes with kv_scale float32
-    [num_pages, 64]); kv_dtype "bf16", "int8" or "fp8".  ``quantize``
+    [num_pages, page_size]); kv_dtype "bf16", "int8" or "fp8".  ``quantize``
     replaces the INT8 quantiser, ``quantize_fp8`` the FP8 one.
     Row j of request b goes to logical position start_pos[b] + j; positions
     outside the request's page table are not written.
@@ -104,13 +105,14 @@ def kv_append(kv_new_bits: np.ndarray, cu_seqlens_new: np.ndarray, start_pos: np
     out = np.array(cache, copy=True)
     sc = None if kv_scale is None else np.array(kv_scale, copy=True)
     max_pages = page_table.shape[1]
+    page_size = cache.shape[1]
     batch = len(start_pos)
     for b in range(batch):
         for j in range(int(cu_seqlens_new[b + 1]) - int(cu_seqlens_new[b])):
             t = int(start_pos[b]) + j
-            if t < 0 or t >= max_pages * 64:
+            if t < 0 or t >= max_pages * page_size:
                 continue
-            page, slot = int(page_table[b, t // 64]), t % 64
+            page, slot = int(page_table[b, t // page_size]), t % page_size
             row = kv_new_bits[int(cu_seqlens_new[b]) + j]
             if kv_dtype == "bf16":
                 out[page, slot] = row

@@ -267,7 +267,7 @@ class PrefillCase:
 
 def make_decode_case(seed: int, batch: int, heads: int, q_len: int, seq_lens=None,
                      len_range=None, kv_dtype: str = "bf16", max_seq_len: Optional[int] = None,
-                     poison: float = POISON_FINITE, name: str = "") -> DecodeCase:
+                     poison: float = POISON_FINITE, name: str = "", page_size: int = PAGE_SIZE) -> DecodeCase:
     """Decode inputs.  Lengths are ``seq_lens`` or drawn uniformly from ``len_range`` (inclusive)."""
     rng = np.random.default_rng(seed)
     if seq_lens is None:
@@ -277,15 +277,16 @@ def make_decode_case(seed: int, batch: int, heads: int, q_len: int, seq_lens=Non
     assert seq_lens.shape == (batch,) and (seq_lens >= q_len).all()
     if max_seq_len is None:
         max_seq_len = int(len_range[1]) if len_range is not None else int(seq_lens.max())
-    max_pages = (max_seq_len + PAGE_SIZE - 1) // PAGE_SIZE
-    cache = build_paged_cache(rng, seed, seq_lens, kv_dtype, max_pages=max_pages, poison=poison)
+    max_pages = (max_seq_len + page_size - 1) // page_size
+    cache = build_paged_cache(rng, seed, seq_lens, kv_dtype, max_pages=max_pages, poison=poison,
+                              page_size=page_size)
     q = draw_query(seed, batch * q_len, heads)
     return DecodeCase(batch, heads, q_len, q, cache, max_seq_len, DEFAULT_SCALE, name)
 
 
 def make_prefill_case(seed: int, heads: int, prefix_lens=None, new_lens=None, batch: int = 0,
                       prefix_range=None, new_range=None, kv_dtype: str = "bf16",
-                      poison: float = POISON_FINITE, name: str = "") -> PrefillCase:
+                      poison: float = POISON_FINITE, name: str = "", page_size: int = PAGE_SIZE) -> PrefillCase:
     """Varlen prefill inputs: request b has prefix_lens[b] cached rows plus new_lens[b] new ones."""
     rng = np.random.default_rng(seed)
     if prefix_lens is None:
@@ -298,8 +299,9 @@ def make_prefill_case(seed: int, heads: int, prefix_lens=None, new_lens=None, ba
     cu = np.zeros(len(new_lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(new_lens)
     max_seq_len = int(kv_lens.max()) if len(kv_lens) else 1
-    max_pages = max(1, (max_seq_len + PAGE_SIZE - 1) // PAGE_SIZE)
-    cache = build_paged_cache(rng, seed, kv_lens, kv_dtype, max_pages=max_pages, poison=poison)
+    max_pages = max(1, (max_seq_len + page_size - 1) // page_size)
+    cache = build_paged_cache(rng, seed, kv_lens, kv_dtype, max_pages=max_pages, poison=poison,
+                              page_size=page_size)
     q = draw_query(seed, int(cu[-1]), heads)
     return PrefillCase(heads, q, cu, prefix_lens, cache, max_seq_len, DEFAULT_SCALE, name)
 

@@ -42,7 +42,7 @@ def run_decode(case, inputs=None, out=None, lse=None, workspace=None, stream=Non
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     mla.mla_decode(d["q"], d["kv"], d["scale"], d["kind"], d["pt"], case.cache.max_pages, d["seq_lens"],
-                   case.batch, case.q_len, H, 64, case.max_seq_len, case.softmax_scale, out, lse, workspace,
+                   case.batch, case.q_len, H, case.cache.page_size, case.max_seq_len, case.softmax_scale, out, lse, workspace,
                    workspace.numel(), stream)
     return out, lse
 
@@ -63,7 +63,8 @@ def run_prefill(case, inputs=None, out=None, lse=None, workspace=None, stream=No
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     mla.mla_prefill_varlen(d["q"], d["cu"], d["prefix"], d["kv"], d["scale"], d["kind"], d["pt"],
-                           case.cache.max_pages, case.batch, T, case.max_q_len(), case.max_seq_len, H, 64,
+                           case.cache.max_pages, case.batch, T, case.max_q_len(), case.max_seq_len, H,
+                           case.cache.page_size,
                            case.softmax_scale, out, lse, workspace, workspace.numel(), stream)
     return out, lse
 
@@ -101,6 +102,7 @@ def run_decode_varlen(case, inputs=None, max_q_len=None, stream=None):
     nbytes = mla.mla_splitkv_workspace_size(case.batch, H, mq, T, case.max_seq_len, d["kind"])
     workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     mla.mla_decode_varlen(d["q"], d["cu"], d["kv"], d["scale"], d["kind"], d["pt"], case.cache.max_pages, lens,
-                          case.batch, T, mq, H, 64, case.max_seq_len, case.softmax_scale, out, lse, workspace,
+                          case.batch, T, mq, H, case.cache.page_size, case.max_seq_len, case.softmax_scale, out,
+                          lse, workspace,
                           workspace.numel(), stream)
     return out, lse

@@ -59,7 +59,11 @@ def _decode_rc(lib, **kw):
     (dict(q_len=0), mla.MLA_ERR_INVALID),
     (dict(heads=0), mla.MLA_ERR_INVALID),
     (dict(page=32), mla.MLA_ERR_UNSUPPORTED),
-    (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page=96), mla.MLA_ERR_UNSUPPORTED),       # not a whole number of 64-row sub-pages
+    (dict(page=8192), mla.MLA_ERR_UNSUPPORTED),     # above the largest page size
+    (dict(page=128), mla.MLA_ERR_WORKSPACE),        # supported: reaches the workspace check
+    (dict(page=1536, maxp=43), mla.MLA_ERR_WORKSPACE),
+    (dict(page=1536, maxp=42), mla.MLA_ERR_INVALID),  # 42 * 1536 rows < max_seq_len
     (dict(kind=3), mla.MLA_ERR_UNSUPPORTED),
     (dict(kind=1), mla.MLA_ERR_INVALID),            # int8 without scales
     (dict(kind=2), mla.MLA_ERR_INVALID),            # fp8 without scales
@@ -150,7 +154,7 @@ def _append_rc(lib, **kw):
     (dict(kind=1), mla.MLA_ERR_INVALID),            # int8 without scales
     (dict(kind=2), mla.MLA_ERR_INVALID),            # fp8 without scales
     (dict(kind=3), mla.MLA_ERR_UNSUPPORTED),
-    (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page=96), mla.MLA_ERR_UNSUPPORTED),
     (dict(total=0, new=None, kv=None), mla.MLA_OK),  # nothing to write, nothing enqueued
 ])
 def test_append_argument_checks(lib, kw, code):
@@ -174,7 +178,7 @@ def _varlen_rc(lib, **kw):
     (dict(mq=0), mla.MLA_ERR_INVALID),
     (dict(mq=9), mla.MLA_ERR_UNSUPPORTED),          # 144 folded rows
     (dict(kind=2), mla.MLA_ERR_INVALID),            # fp8 without scales
-    (dict(page=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page=96), mla.MLA_ERR_UNSUPPORTED),
     (dict(maxlen=3), mla.MLA_ERR_INVALID),
     (dict(ws=None, wsb=0), mla.MLA_ERR_WORKSPACE),
     (dict(tq=0), mla.MLA_OK),                       # nothing to do, no launch

@@ -180,3 +180,35 @@ def _first_request_table(new, cu, start, cache, scale, kv_dtype, pt):
 def test_placement_mutants_fail(mutant):
     with pytest.raises(AssertionError):
         _check_placement(mutant, "bf16")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("page_size", [128, 1536])
+def test_placement_any_page_size(kv_dtype, page_size):
+    """A page of P rows is P / 64 consecutive 64-row pages: appending into a P-row cache
+    equals appending into the same memory seen as 64-row pages through the expanded table."""
+    rng = np.random.default_rng(71)
+    k = page_size // 64
+    batch, entries = 2, 3
+    num_pages = batch * entries + 1
+    pt = rng.permutation(num_pages)[: batch * entries].reshape(batch, entries).astype(np.int32)
+    if kv_dtype == "bf16":
+        cache = rng.integers(0, 1 << 16, size=(num_pages, page_size, 576), dtype=np.uint16)
+        scale = None
+    else:
+        cache = rng.integers(-127, 128, size=(num_pages, page_size, 576), dtype=np.int8)
+        if kv_dtype == "fp8":
+            cache = cache.view(np.uint8)
+        scale = rng.random((num_pages, page_size), dtype=np.float32)
+    start = np.array([page_size - 5, 3], np.int32)
+    n = np.array([70, 9], np.int32)
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    new = synth.bf16_bits(rng.standard_normal((int(cu[-1]), 576)).astype(np.float32))
+    big, big_sc = oracle.kv_append(new, cu, start, cache, scale, kv_dtype, pt)
+    pt64 = (pt[:, :, None] * k + np.arange(k)[None, None, :]).reshape(batch, entries * k).astype(np.int32)
+    small, small_sc = oracle.kv_append(new, cu, start, cache.reshape(num_pages * k, 64, 576),
+                                       None if scale is None else scale.reshape(num_pages * k, 64), kv_dtype, pt64)
+    assert np.array_equal(big.reshape(num_pages * k, 64, 576), small)
+    if scale is not None:
+        assert np.array_equal(big_sc.reshape(num_pages * k, 64), small_sc)
+    assert not np.array_equal(big, cache)                 # something was written
