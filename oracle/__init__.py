@@ -6,7 +6,8 @@ leg may import this package.  The library's compute path never does.
 ``mla_oracle.c`` holds the definition (see its header for the passages it
 follows); this module compiles it with gcc when the shared object is missing
 or older than the source, and wraps it with ctypes.  ``kv_append.py`` is the
-oracle of the step that writes new tokens' rows into the pages.
+oracle of the step that writes new tokens' rows into the pages; ``absorb.py``
+that of the query absorption and value up-projection around the attention.
 """
 from __future__ import annotations
 
@@ -148,3 +149,4 @@ def e4m3_value(code: int) -> float:
 
 
 from .kv_append import kv_append, quantize_row, quantize_row_fp8, e4m3_round  # noqa: E402
+from . import absorb  # noqa: E402  (the products on either side of the absorbed attention)
