@@ -202,6 +202,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-absorb", action="store_true",
+                    help="skip the query-absorption / value up-projection leg")
     ap.add_argument("--no-pages", action="store_true",
                     help="skip the page-size leg (the 64K decode with 128- and 1536-row pages)")
     ap.add_argument("--no-varlen", action="store_true",
@@ -320,6 +322,29 @@ def main() -> int:
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
         }
+
+    # ---------------- absorption and up-projection on the prefill workload's tokens ----------------
+    if not args.no_absorb:
+        AT, AH = 8629, 16
+        g = torch.Generator(device="cuda").manual_seed(11)
+        aq = torch.randn((AT, AH, 192), generator=g, device="cuda").to(torch.bfloat16)
+        wuk = (torch.randn((AH, 512, 128), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+        wuv = (torch.randn((AH, 128, 512), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+        aout = torch.empty((AT, AH, 576), dtype=torch.bfloat16, device="cuda")
+        ao = torch.randn((AT, AH, 512), generator=g, device="cuda").to(torch.bfloat16)
+        vout = torch.empty((AT, AH, 128), dtype=torch.bfloat16, device="cuda")
+        legs = {}
+        for name, fn in (("q_absorb", lambda: mla.mla_q_absorb(aq, wuk, aout, AT, AH, stream)),
+                         ("v_up", lambda: mla.mla_v_up(ao, wuv, vout, AT, AH, stream))):
+            n = 200
+            ms = time_calls([fn], stream, 2000, n) / n
+            fl = 2 * AT * AH * 128 * 512
+            legs[name] = {"us_per_call": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                          "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "flops_per_call": fl}
+        result["absorb"] = {"workload": f"{AT} tokens x {AH} heads (the prefill workload's new tokens)",
+                            "kernel": "nt_gemm (bf16 MFMA)", "bound": "mfma", **legs}
+        del aq, wuk, wuv, aout, ao, vout
+        torch.cuda.empty_cache()
 
     # ---------------- page sizes: the 64K decode with 128- and 1536-row pages ----------------
     if not args.no_pages:

@@ -103,6 +103,9 @@ extern "C" {
 
 #define MLA_DIM_QK 576      /* cache row / query row width: 512 latent + 64 rope */
 #define MLA_DIM_V 512       /* value width: the first 512 columns of a row */
+#define MLA_DIM_NOPE 128    /* per-head query / key width without position (unabsorbed) */
+#define MLA_DIM_ROPE 64     /* per-head rotary part, shared by query and cache row */
+#define MLA_DIM_VHEAD 128   /* per-head value width after the up-projection */
 #define MLA_PAGE_SIZE 64    /* the kernels' sub-page: page sizes are multiples of it */
 #define MLA_MAX_PAGE_SIZE 4096 /* largest page size */
 #define MLA_MAX_DECODE_ROWS 128 /* q_len * num_heads of one decode request */
@@ -278,6 +281,42 @@ int mla_prefill_varlen(const void* q, const int32_t* cu_seqlens_q, const int32_t
 int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32_t* start_pos,
                   void* kv_cache, float* kv_scale, int kv_dtype, const int32_t* page_table,
                   int max_pages_per_req, int batch, int total_new, int page_size, void* hip_stream);
+
+/*
+ * Query absorption: q_out[t][h] = [W_UK[h]^T q_nope[t][h] ; q_rope[t][h]], the
+ * 576-wide query the attention entry points take [TALK, section
+ * "Kernel：让 MLA 真正跑满 GPU": attention over compressed latent rows, query
+ * x latent key; the absorbed form is the published MLA formulation: per head
+ * the key without position is W_UK[h] c for the latent row c, so
+ * q_nope . (W_UK[h] c) = (W_UK[h]^T q_nope) . c].
+ *
+ *   q        bf16 [tokens, num_heads, 192]: q_nope (128) | q_rope (64)
+ *   w_uk_t   bf16 [num_heads, 512, 128]: W_UK[h] transposed (row c holds
+ *            W_UK[h][0..127][c]), so that both operands are contiguous in
+ *            the contracted index
+ *   q_out    bf16 [tokens, num_heads, 576]: 512 absorbed values (fp32
+ *            accumulation, rounded to nearest even) then q_rope unchanged
+ *
+ * Returns MLA_OK (tokens == 0 enqueues nothing), MLA_ERR_INVALID for a null
+ * pointer (tokens > 0), tokens < 0 or num_heads < 1, MLA_ERR_UNSUPPORTED when
+ * tokens * num_heads * 576 overflows int32, MLA_ERR_HIP.
+ */
+int mla_q_absorb(const void* q, const void* w_uk_t, void* q_out, int tokens, int num_heads, void* hip_stream);
+
+/*
+ * Value up-projection: out[t][h] = W_UV[h] o_lat[t][h], the head output from
+ * the 512-wide latent attention output [MLA: the value of a token is W_UV[h] c
+ * for its latent row c, and attention weights sum linearly, so the head
+ * output is W_UV[h] applied to the weighted mean of latent rows].
+ *
+ *   o_lat    bf16 [tokens, num_heads, 512] (the attention entry points' out)
+ *   w_uv     bf16 [num_heads, 128, 512]: W_UV[h][v][c]
+ *   out      bf16 [tokens, num_heads, 128] (fp32 accumulation, rounded to
+ *            nearest even)
+ *
+ * Returns as mla_q_absorb.
+ */
+int mla_v_up(const void* o_lat, const void* w_uv, void* out, int tokens, int num_heads, void* hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(int status);

@@ -58,6 +58,10 @@ def library():
         lib.mla_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
                                            f32, vp, vp, vp, sz, vp]
         lib.mla_prefill_varlen.restype = i32
+        lib.mla_q_absorb.argtypes = [vp, vp, vp, i32, i32, vp]
+        lib.mla_q_absorb.restype = i32
+        lib.mla_v_up.argtypes = [vp, vp, vp, i32, i32, vp]
+        lib.mla_v_up.restype = i32
         lib.mla_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp]
         lib.mla_kv_append.restype = i32
         lib.mla_status_string.argtypes = [i32]
@@ -129,6 +133,16 @@ def mla_decode_varlen(q, cu_seqlens_q, kv_cache, kv_scale, kv_dtype, page_table,
                                      _ptr(out), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                      _stream(hip_stream))
     _check(rc, "mla_decode_varlen")
+
+
+def mla_q_absorb(q, w_uk_t, q_out, tokens, num_heads, hip_stream=None) -> None:
+    _check(library().mla_q_absorb(_ptr(q), _ptr(w_uk_t), _ptr(q_out), tokens, num_heads, _stream(hip_stream)),
+           "mla_q_absorb")
+
+
+def mla_v_up(o_lat, w_uv, out, tokens, num_heads, hip_stream=None) -> None:
+    _check(library().mla_v_up(_ptr(o_lat), _ptr(w_uv), _ptr(out), tokens, num_heads, _stream(hip_stream)),
+           "mla_v_up")
 
 
 def mla_prefill_varlen(q, cu_seqlens_q, prefix_lens, kv_cache, kv_scale, kv_dtype, page_table,

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libmla.so")
-SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_prefill.hip", "mla_append.hip"]
+SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_prefill.hip", "mla_append.hip", "mla_gemm.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -378,4 +378,56 @@ int mla_kv_append(const void* kv_new, const int32_t* cu_seqlens_new, const int32
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_q_absorb(const void* q, const void* w_uk_t, void* q_out, int tokens, int num_heads, void* hip_stream) {
+  if (tokens < 0 || num_heads < 1) return MLA_ERR_INVALID;
+  if (tokens == 0) return MLA_OK;
+  if (!q || !w_uk_t || !q_out) return MLA_ERR_INVALID;
+  if ((long long)tokens * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
+  const size_t dq = MLA_DIM_NOPE + MLA_DIM_ROPE;
+  GemmArgs g{};
+  g.a = static_cast<const uint16_t*>(q);
+  g.a_row = (size_t)num_heads * dq;
+  g.a_head = dq;
+  g.bt = static_cast<const uint16_t*>(w_uk_t);
+  g.b_row = MLA_DIM_NOPE;
+  g.b_head = (size_t)MLA_DIM_V * MLA_DIM_NOPE;
+  g.c = static_cast<uint16_t*>(q_out);
+  g.c_row = (size_t)num_heads * MLA_DIM_QK;
+  g.c_head = MLA_DIM_QK;
+  g.m = tokens;
+  g.n = MLA_DIM_V;
+  g.k = MLA_DIM_NOPE;
+  g.rope_src = g.a + MLA_DIM_NOPE;
+  g.rope_src_row = g.a_row;
+  g.rope_src_head = g.a_head;
+  g.rope_dst = g.c + MLA_DIM_V;
+  g.rope_dst_row = g.c_row;
+  g.rope_dst_head = g.c_head;
+  g.rope_cols = MLA_DIM_ROPE;
+  const hipError_t e = launch_gemm(g, num_heads, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_v_up(const void* o_lat, const void* w_uv, void* out, int tokens, int num_heads, void* hip_stream) {
+  if (tokens < 0 || num_heads < 1) return MLA_ERR_INVALID;
+  if (tokens == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID;
+  if ((long long)tokens * num_heads > 0x7fffffffLL / MLA_DIM_QK) return MLA_ERR_UNSUPPORTED;
+  GemmArgs g{};
+  g.a = static_cast<const uint16_t*>(o_lat);
+  g.a_row = (size_t)num_heads * MLA_DIM_V;
+  g.a_head = MLA_DIM_V;
+  g.bt = static_cast<const uint16_t*>(w_uv);
+  g.b_row = MLA_DIM_V;
+  g.b_head = (size_t)MLA_DIM_VHEAD * MLA_DIM_V;
+  g.c = static_cast<uint16_t*>(out);
+  g.c_row = (size_t)num_heads * MLA_DIM_VHEAD;
+  g.c_head = MLA_DIM_VHEAD;
+  g.m = tokens;
+  g.n = MLA_DIM_VHEAD;
+  g.k = MLA_DIM_V;
+  const hipError_t e = launch_gemm(g, num_heads, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 }  // extern "C"

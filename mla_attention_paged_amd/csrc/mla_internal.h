@@ -76,6 +76,24 @@ struct AppendArgs {
   int code;                   // scaled caches: 1 INT8, 2 FP8 (E4M3)
 };
 
+// One NT product per head: C[m][n] = sum_k A[m][k] Bt[n][k]; element strides.
+// With rope_cols > 0, the workgroups of the first column tile also copy
+// rope_cols values per row from rope_src to rope_dst.
+struct GemmArgs {
+  const uint16_t* a;
+  size_t a_row, a_head;
+  const uint16_t* bt;
+  size_t b_row, b_head;
+  uint16_t* c;
+  size_t c_row, c_head;
+  int m, n, k;                // n: a multiple of 64; k: a multiple of 32
+  const uint16_t* rope_src;
+  size_t rope_src_row, rope_src_head;
+  uint16_t* rope_dst;
+  size_t rope_dst_row, rope_dst_head;
+  int rope_cols;              // a multiple of 8, or 0
+};
+
 struct DecodePlan {
   int grid;                   // phase-one workgroups (1: single pass, no merge)
   int waves;                  // waves per workgroup (4 or 8)
@@ -98,5 +116,6 @@ PrefillPlan plan_prefill(int batch, int heads, int max_q_len, int total_q, int m
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& args, int kv_dtype, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& g, int heads, hipStream_t stream);
 
 }  // namespace mla

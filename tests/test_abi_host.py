@@ -191,3 +191,15 @@ def test_workspace_covers_varlen_decode(lib):
     # fewer tokens than batch * max_q_len still sizes the decode split
     ws = mla.mla_splitkv_workspace_size(4, 16, 4, 10, 65536, 0)
     assert ws >= mla.mla_decode_plan(4, 16, 4, 65536, 0, num_cus=256)[1]
+
+
+@pytest.mark.parametrize("fn", ["mla_q_absorb", "mla_v_up"])
+def test_absorb_argument_checks(lib, fn):
+    f = getattr(lib, fn)
+    assert f(1, 1, 1, -1, 16, None) == mla.MLA_ERR_INVALID
+    assert f(1, 1, 1, 4, 0, None) == mla.MLA_ERR_INVALID
+    assert f(None, 1, 1, 4, 16, None) == mla.MLA_ERR_INVALID
+    assert f(1, None, 1, 4, 16, None) == mla.MLA_ERR_INVALID
+    assert f(1, 1, None, 4, 16, None) == mla.MLA_ERR_INVALID
+    assert f(None, None, None, 0, 16, None) == mla.MLA_OK        # nothing to do, no launch
+    assert f(1, 1, 1, 1 << 30, 16, None) == mla.MLA_ERR_UNSUPPORTED
