@@ -110,9 +110,12 @@ def time_calls(fn_list, stream, warmup: int, steps: int) -> float:
     return t0.elapsed_time(t1)
 
 
+# the sources that shape the decode call's kernels and plan (its recorded HBM traffic is
+# dropped when any of them changes)
 KERNEL_SOURCES = ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_decode.hip",
-                  "mla_attention_paged_amd/csrc/mla_prefill.hip", "mla_attention_paged_amd/csrc/mla_device.h",
-                  "mla_attention_paged_amd/csrc/mla_internal.h"]
+                  "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h"]
+COUNTER_RUN_FLAGS = ("--steps 5 --warmup 20 --no-prefill --no-append --no-cpu-baseline --no-absorb --no-pages "
+                     "--no-varlen --no-scaled")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_decode_b4_h16_q4_L64K_traffic.json")
 
 
@@ -181,9 +184,9 @@ def record_traffic(fetch_dir: str, write_dir: str, calib_mb: int) -> int:
            "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
            "calibration": f"plain device copy of {calib_mb} MiB (torch copy_), largest copy dispatch reading",
            "commands": [f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -f csv -d {fetch_dir} -o fetch -- "
-                        f"python3 bench.py --steps 5 --no-prefill --no-append --no-cpu-baseline --calib-copy-mb {calib_mb}",
+                        f"python3 bench.py {COUNTER_RUN_FLAGS} --calib-copy-mb {calib_mb}",
                         f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -f csv -d {write_dir} -o write -- "
-                        f"python3 bench.py --steps 5 --no-prefill --no-append --no-cpu-baseline --calib-copy-mb {calib_mb}",
+                        f"python3 bench.py {COUNTER_RUN_FLAGS} --calib-copy-mb {calib_mb}",
                         f"python3 bench.py --record-traffic {fetch_dir} {write_dir} --calib-copy-mb {calib_mb}"]}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
