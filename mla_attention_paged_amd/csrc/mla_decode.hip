@@ -84,6 +84,51 @@ __device__ __forceinline__ void flush_rows(const DecodeArgs& a, const RowState& 
   }
 }
 
+// The last flush of a workgroup, through LDS: every wave's normalised bf16
+// rows go, row-major with a 1040-byte pitch, into `buf` (the idle ring),
+// and then each wave stores whole 1 KB rows of the block (rows 8w .. 8w+7
+// that the request has: nrows of them), so every store instruction fills
+// eight 128-byte lines instead of touching sixteen lines 32 bytes at a time.
+// All waves of the workgroup call it (barriers inside).
+constexpr int kFlushPitch = kDv * 2 + 16;
+
+__device__ __forceinline__ void flush_rows_lds(const DecodeArgs& a, const RowState& st, int tok0, int slot,
+                                               int nrows, int row, bool row_ok, bool wave_rows, int half, int w,
+                                               int lane, MLA_LDS uint8_t* buf) {
+  lds_barrier();  // every wave is done reading the ring
+  if (wave_rows) {
+    float inv, lse2;
+    finish_row(st, inv, lse2);
+    const int g = lane >> 4;
+    MLA_LDS uint8_t* dst = buf + (16 * (w & 3) + (lane & 15)) * kFlushPitch + 2 * ((kDv / 2) * half + 4 * g);
+#pragma unroll
+    for (int ct = 0; ct < kOHalf; ++ct) {
+      const f32x4 v = st.o[ct] * inv;
+      bf16x4 h;
+      h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+      *reinterpret_cast<MLA_LDS bf16x4*>(dst + 32 * ct) = h;
+    }
+    if (row_ok && g == 0 && half == 0) {
+      if (a.grid == 1)
+        a.lse[(size_t)tok0 * a.heads + row] = lse2 * kLn2;
+      else
+        a.part_lse[(size_t)slot * a.rows + row] = lse2;
+    }
+  }
+  lds_write_barrier();
+  const int r0 = kBlockRows * blockIdx.y;
+  uint16_t* const base = a.grid == 1 ? a.out + ((size_t)tok0 * a.heads + r0) * kDv
+                                     : a.part_o + ((size_t)slot * a.rows + r0) * kDv;
+#pragma unroll
+  for (int k = 0; k < kBlockRows / kWaves; ++k) {
+    const int rr = (kBlockRows / kWaves) * w + k;
+    if (rr < nrows) {
+      const bf16x8 x = *reinterpret_cast<const MLA_LDS bf16x8*>(buf + rr * kFlushPitch + 16 * lane);
+      *reinterpret_cast<bf16x8*>(base + (size_t)rr * kDv + 8 * lane) = x;
+    }
+  }
+}
+
 // Clamped request lengths, cached in LDS for the first kLenCache requests
 // (the tile-list walks read them repeatedly; the cache keeps those reads
 // off the global-memory latency chain in front of the first tile).
@@ -265,13 +310,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   RowState st;
   bf16x8 qf[kQFrags];
   int cur_b = -1;
-  // The first request's query loads start now, overlapping the tile-list
-  // fill and the first tile; the first tile's wait covers them.
-  int q_b = -1;  // request whose query fragments are loaded or in flight
-  if (wave_rows && cb < a.batch) {
-    set_req(cb);
-    issue_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
-    q_b = cb;
+  // The first request's query block streams into ring stages 1-2 (free
+  // until the first step issues tile 1) in whole-line direct-to-LDS loads,
+  // issued by waves 1-7 while wave 0 fills the tile list; the first step's
+  // wait covers them and the first step moves the block into registers.
+  // (Per-lane fragment loads from HBM touch every line twice, half a line at
+  // a time, and took several microseconds here; the same loads issued after
+  // the first tile's delay that tile by about 2 us.)
+  const int q_b = cb;  // request whose query block is staged
+  bool q_staged = true;
+  if (w > 0) {
+    const ReqQ r = req_q(a, s_tok, q_b);
+    const int nrows = min(r.n * a.heads - kBlockRows * (int)blockIdx.y, kBlockRows);
+    if (nrows > 0)
+      stage_q(a.q + ((size_t)r.tok0 * a.heads + kBlockRows * blockIdx.y) * kDqk, nrows, stage(1), w - 1,
+              kWaves - 1, lane);
   }
 
   for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
@@ -293,13 +346,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
         if (cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
         set_req(b);
         if (b != q_b) load_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
-        q_b = -1;
         reset_state(st);
       }
       cur_b = b;
       // first step: scores only
       wait_vmcnt<0>();
       lds_write_barrier();
+      if (q_staged) {  // the first request's block, then free stages 1-2 for the ring
+        if (wave_rows) read_q(stage(1), w & 3, lane, row_ok, qf);
+        lds_write_barrier();
+        q_staged = false;
+      }
       if (t0 + 1 < N) issue(t0 + 1);
       f32x4 s_prev = {0.f, 0.f, 0.f, 0.f};
       if (wave_rows) {
@@ -335,7 +392,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
       t0 = t1;
     }
   }
-  if (wave_rows && cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
+  if (cur_b >= 0) {
+    const ReqQ r = req_q(a, s_tok, cur_b);
+    const int nrows = min(r.n * a.heads - kBlockRows * (int)blockIdx.y, kBlockRows);
+    flush_rows_lds(a, st, r.tok0, g + cur_b, nrows, row, row_ok, wave_rows, half, w, lane, ring);
+  }
 }
 
 // Phase one for an INT8 or FP8 cache (CODE), software-pipelined like the
@@ -484,13 +545,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs
 // Phase two: per (request, row), reduce the partials of the workgroups
 // whose shares intersect the request: lse = log2-sum-exp of the partial
 // lses, out = sum_s 2^(lse_s - lse) o_s.  One workgroup per (row, quarter of
-// the value columns).  The share weights 2^(lse_s - m) are computed once
-// into LDS (m: the max partial lse; empty shares weigh 0); then thread
-// (group j, quad c) accumulates shares j, j + 8, ... for columns 4c .. 4c+3
-// of the quarter, with all its loads of a batch of shares in flight at once,
-// and the eight groups are combined through LDS.  Empty shares read the
-// first share's (written, finite) slot with weight 0, so bytes of the
-// workspace that phase one did not write never enter the sums.
+// the value columns); thread (group j, quad c) accumulates shares j, j + 8,
+// ... for columns 4c .. 4c+3 of the quarter, eight partial loads in flight
+// at once, and the eight groups are combined through LDS.  Two dependent
+// memory round trips: the page offsets (with the query offsets), then each
+// thread's share lse (thread i: share i) together with its group's first
+// eight partials; the block max m of the lses and the weights 2^(lse_s - m)
+// (0 for empty shares) then come from registers and LDS.  Requests with more
+// than 64 shares load further batches of partials; more than 256 (a grid
+// beyond 256 workgroups) reload the lses of each later chunk of 256.  Empty
+// shares read the first share's (written, finite) slot with weight 0, so
+// bytes of the workspace that phase one did not write never enter the sums.
 constexpr int kMergeGroups = 8;
 constexpr int kMergeChunk = 256;  // share weights held in LDS at a time
 
@@ -509,59 +574,73 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int R = blockIdx.x;
   const int quarter = blockIdx.y;
   const int b = R / a.rows, row = R - b * a.rows;
-  int tok0 = b * a.q_len;
+  // round trip 1: page offsets and query offsets, loaded together
+  const long long P = a.cum_pages[a.batch];
+  const long long p0 = a.cum_pages[b], p1 = a.cum_pages[b + 1];
+  int tok0 = b * a.q_len, nq = a.q_len;
   if (a.cu_q) {
     tok0 = a.cu_q[b];
-    if (row >= (a.cu_q[b + 1] - tok0) * a.heads) return;  // a row the request does not have
+    nq = a.cu_q[b + 1] - tok0;
   }
-  const size_t orow = (size_t)tok0 * a.heads + row;     // output row
-  const long long P = a.cum_pages[a.batch];
-  const int G = a.grid;
-  const long long p0 = a.cum_pages[b], p1 = a.cum_pages[b + 1];
+  if (row >= nq * a.heads) return;  // a row the request does not have
   if (p1 <= p0) return;
+  const size_t orow = (size_t)tok0 * a.heads + row;  // output row
+  const int G = a.grid;
   const int g0 = owner_group(p0, P, G), g1 = owner_group(p1 - 1, P, G);
   const int ns = g1 - g0 + 1;
   const float* lse_col = a.part_lse + (size_t)(g0 + b) * a.rows + row;  // share i: lse_col[i * rows]
 
-  float m = -INFINITY;
-  for (int i = tid; i < ns; i += 256)
-    if (!share_empty(P, G, g0 + i)) m = fmaxf(m, lse_col[(size_t)i * a.rows]);
+  const int grp = tid >> 5, quad = tid & 31;
+  const int col = quarter * (kDv / 4) + 4 * quad;
+  const uint16_t* o_col = a.part_o + ((size_t)(g0 + b) * a.rows + row) * kDv + col;  // share i: + i * rows * 512
+  const size_t share_stride = (size_t)a.rows * kDv;
+  // shares can be empty only when there are fewer pages than workgroups
+  const bool sparse = P < G;
+  auto has_share = [&](int i) { return i < ns && (!sparse || !share_empty(P, G, g0 + i)); };
+  auto share_lse = [&](int i) { return has_share(i) ? lse_col[(size_t)i * a.rows] : -INFINITY; };
+  // the partials of shares k, k + 8, ..., k + 56 (the first share's slot where a share is missing or empty)
+  auto load_batch = [&](int k, f32x4 (&v)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = k + u * kMergeGroups;
+      const int src = has_share(i) ? i : 0;
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(o_col + (size_t)src * share_stride);
+      v[u] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+  };
+
+  // round trip 2: this thread's share lses and its group's first batch of partials
+  const float l_own = share_lse(tid);
+  f32x4 v[8];
+  load_batch(grp, v);
+  float m = l_own;
+  for (int i = tid + kMergeChunk; i < ns; i += kMergeChunk) m = fmaxf(m, share_lse(i));
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
   if (lane == 0) s_red[w] = m;
   __syncthreads();
   m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float m_use = m == -INFINITY ? 0.f : m;
+  s_wgt[tid] = fast_exp2(l_own - m_use);  // 0 past the shares and for empty ones
 
-  const int grp = tid >> 5, quad = tid & 31;
-  const int col = quarter * (kDv / 4) + 4 * quad;
-  const uint16_t* o_col = a.part_o + ((size_t)(g0 + b) * a.rows + row) * kDv + col;  // share i: + i * rows * 512
-  const size_t share_stride = (size_t)a.rows * kDv;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
+  bool loaded = true;  // v holds shares grp, grp + 8, ... of the first chunk
   for (int c0 = 0; c0 < ns; c0 += kMergeChunk) {
     const int nc = min(kMergeChunk, ns - c0);
-    __syncthreads();  // the previous chunk's weights are no longer read
-    if (tid < nc) {
-      const int i = c0 + tid;
-      s_wgt[tid] = share_empty(P, G, g0 + i) ? 0.f : fast_exp2(lse_col[(size_t)i * a.rows] - m_use);
+    if (c0 > 0) {
+      __syncthreads();  // the previous chunk's weights are no longer read
+      s_wgt[tid] = fast_exp2(share_lse(c0 + tid) - m_use);
     }
     __syncthreads();
     for (int k0 = grp; k0 < nc; k0 += 8 * kMergeGroups) {
-      f32x4 v[8];
-      float wt[8];
+      if (!loaded) load_batch(c0 + k0, v);
+      loaded = false;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * kMergeGroups;
-        wt[u] = k < nc ? s_wgt[k] : 0.f;
-        const int i = wt[u] > 0.f ? c0 + k : 0;  // zero weight: the first share's slot
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(o_col + (size_t)i * share_stride);
-        v[u] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc += v[u] * wt[u];
-        wsum += wt[u];
+        const float wt = s_wgt[k0 + u * kMergeGroups];  // k0 + 8u < 256: 0 past the chunk's shares
+        acc += v[u] * wt;
+        wsum += wt;
       }
     }
   }

@@ -356,6 +356,43 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, int la
   wait_vmcnt<0>();
 }
 
+// A workgroup's 64-row query block staged in LDS: row r's 16-byte chunk c
+// sits in slot 72 r + (c ^ ((r >> 1) & 7)).  The XOR keeps c inside its
+// group of eight chunks; it spreads the 16 rows of one fragment read over
+// all 16 bank groups (the unswizzled 1152-byte pitch puts every other row
+// on the same banks).
+constexpr int kQLoads = kBlockRows * kRowChunks / 64;  // 72 wave-wide loads
+
+__device__ __forceinline__ int q_slot(int r, int c) { return kRowChunks * r + (c ^ ((r >> 1) & 7)); }
+
+// Issue loads i = first, first + step, ... of the block's direct-to-LDS
+// loads that hold rows 0 .. nrows - 1 of `qblk` (1 <= nrows <= 64), in whole
+// 1 KB wave loads.  Slots of the last load past row nrows - 1 repeat it, so
+// nothing past the block's rows is read; later rows stay unwritten (their
+// fragments are zeroed on reading).
+__device__ __forceinline__ void stage_q(const uint16_t* __restrict__ qblk, int nrows, MLA_LDS uint8_t* dst,
+                                        int first, int step, int lane) {
+  const int loads = (nrows * kRowChunks + 63) / 64;
+  for (int i = first; i < loads; i += step) {
+    const int sl = i * 64 + lane;
+    const int r = sl / kRowChunks;
+    const int c = (sl - r * kRowChunks) ^ ((r >> 1) & 7);
+    lds_dma16(reinterpret_cast<const uint8_t*>(qblk), (r < nrows ? r : nrows - 1) * kRowBytes + c * 16,
+              dst + i * 1024);
+  }
+}
+
+// This wave's Q fragments (block rows 16 rg .. 16 rg + 15, the layout of
+// load_q) from a staged block; zero where `ok` is false.
+__device__ __forceinline__ void read_q(const MLA_LDS uint8_t* src, int rg, int lane, bool ok,
+                                       bf16x8 (&qf)[kQFrags]) {
+  const int r = 16 * rg + (lane & 15);
+  const int g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < kQFrags; ++ks)
+    qf[ks] = ok ? *reinterpret_cast<const MLA_LDS bf16x8*>(src + 16 * q_slot(r, 4 * ks + g)) : bf16x8{};
+}
+
 // Scores may run this far (log2 units) above the running max before the
 // max is raised and the accumulators rescaled.  The result is the same (the
 // final normalisation uses the same stale max); it only bounds the
