@@ -20,6 +20,8 @@
 // time first).  Every tile streams its request's pages 0 .. through the same
 // LDS pipeline as decode; only the pages that hold a row some query token of
 // the tile can see are read, and only the diagonal pages are masked.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -224,39 +226,374 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_codes(Prefi
   }
 }
 
-// bf16 cache: the pipelined core over a ring of four stages, two tiles in
-// flight.  Step k of a window waits for tile k, passes a barrier, starts
-// tile k + 2, and computes the scores of tile k while the softmax and value
-// product of tile k - 1 run in the same basic block.  The partner waves swap
-// score halves through one slot per wave: the slot of tile k - 1 is read
-// right after the first barrier, and a second barrier at the end of the
-// step orders those reads before the slot is overwritten with tile k.  (The
-// double-buffered slot of the decode kernel would not fit beside a fourth
-// stage in 160 KB of LDS; a third stage only, with one tile in flight,
-// leaves the tile's load latency exposed: measured 19% slower.)
+// bf16 cache: a ring of four stages, two tiles in flight while two are read
+// (tile k by the score waves, tile k - 1 by the value waves).  A third stage
+// only, with one tile in flight, left the tile's load latency exposed in an
+// earlier design (19% slower).
 constexpr int kPFStages = 4;
 
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_bf16(PrefillArgs a) {
+// ---------------------------------------------------------------------------
+// Wave-specialised bf16 prefill.  Waves 0-3 compute scores and softmax,
+// waves 4-7 the value product (waves w and w + 4 share a SIMD).  The 64
+// query rows of a work tile form two 32-row groups rg.  Score wave (rg, kh)
+// holds the query fragments of its group's rows (two 16-row MFMA tiles)
+// and scores them against rows 16kh .. 16kh+15 of each staged tile, so each
+// K fragment read from LDS feeds two MFMAs.  Value wave (rg, ch) holds the
+// accumulators of the same 32 rows for value columns 256ch .. 256ch+255, so
+// each transposed V fragment read feeds two MFMAs.  Per 32-row tile the
+// waves read 74 KB of K and 66 KB of V from LDS, half of what four 16-row
+// groups that each read the whole tile need; the MFMA work per SIMD is the
+// same.
+//
+// Step k (between barriers B1(k) and B2(k), then B2(k) to B1(k+1)):
+//  - score waves: take the partner's row max of tile k-1 (written after
+//    B2(k-1)), finish the softmax of tile k-1 for their own 16 rows of it
+//    (the two partners use the same max, so they make the same rescale
+//    decisions), write their half of the probability fragments and the
+//    rescale factors, and compute the scores of tile k (the first six K
+//    fragments are requested before the softmax, which covers their
+//    latency); after B2(k) they publish tile k's row max;
+//  - value waves: before B2(k), while the score waves work, request all 32
+//    transposed V fragments of tile k-1 (64 registers); after B2(k),
+//    rescale and run the value product's 32 MFMAs back to back.
+// Each phase has one active wave per SIMD, so each wave hides its own LDS
+// latency: measured, the fetch-ahead made the kernel 9% faster.
+// Each score wave keeps the row sums of its own 16 rows of every tile; the
+// two halves are added at the end of the work tile.  Stages k (scores) and
+// k-1 (values) are read during step k while k+1 and k+2 load.
+// ---------------------------------------------------------------------------
+
+// Scores of this wave's 16 tile rows against two 16-row query tiles: each K
+// fragment is read once and used by both tiles' MFMAs (four accumulator
+// chains).  s_j[e]: tile row 16kh + 4(lane>>4) + e, query row lane & 15 of
+// query tile j.
+__device__ __forceinline__ void scores_2q(const MLA_LDS uint8_t* tile, const bf16x8 (&q0)[kQFrags],
+                                          const bf16x8 (&q1)[kQFrags], int lane, int kh, f32x4& s0, f32x4& s1) {
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const MLA_LDS uint8_t* kbase = tile + tile_off(16 * kh + r16, g);
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
+  bf16x8 kb[kKDepth + 1];
+#pragma unroll
+  for (int d = 0; d < kKDepth; ++d) kb[d] = lds_b128(kbase + 64 * d);
+#pragma unroll
+  for (int ks = 0; ks < kQFrags; ++ks) {
+    if (ks + kKDepth < kQFrags) kb[(ks + kKDepth) % (kKDepth + 1)] = lds_b128(kbase + 64 * (ks + kKDepth));
+    const bf16x8 kf = kb[ks % (kKDepth + 1)];
+    if (ks & 1) {
+      a1 = mfma16x16x32(kf, q0[ks], a1);
+      b1 = mfma16x16x32(kf, q1[ks], b1);
+    } else {
+      a0 = mfma16x16x32(kf, q0[ks], a0);
+      b0 = mfma16x16x32(kf, q1[ks], b0);
+    }
+  }
+  s0 = a0 + a1;
+  s1 = b0 + b1;
+}
+
+// Scale to log2 units and mask (tile row tt visible when tt <= lim); returns
+// the row max over the wave's 16 tile rows (equal on the row's four lanes).
+__device__ __forceinline__ float mask_half(f32x4 acc, int kh, int lim, float scale_log2, int lane, f32x4& s) {
+  const int g = lane >> 4;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = 16 * kh + 4 * g + e <= lim ? acc[e] * scale_log2 : -INFINITY;
+    s[e] = v;
+    mx = fmaxf(mx, v);
+  }
+  return wave_max_rows(mx);
+}
+
+// Online softmax of this wave's 16 rows of a tile, given the row max over
+// all 32 (mx): raises the running max m past the slack, returns the four
+// probabilities (bf16, the wave's half of the value product's B operand)
+// and the factor alpha for the accumulators; lh is this lane's share of the
+// row sum over the wave's rows of every tile.
+__device__ __forceinline__ bf16x4 softmax_half(const f32x4& s, float mx, float& m, float& lh, float& alpha) {
+  const float m_new = mx > m + kRescaleSlack ? mx : m;
+  alpha = m_new == m ? 1.f : fast_exp2(m - m_new);
+  m = m_new;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  bf16x4 p;
+  float ps = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = fast_exp2(s[e] - m_use);
+    ps += v;
+    p[e] = (__bf16)v;
+  }
+  lh = lh * alpha + ps;
+  return p;
+}
+
+// The value waves' two parts of a tile's value product: all 32 transposed V
+// fragments of the wave's 256 columns (issued while the score waves work,
+// into 64 registers), then the 32 MFMAs for the two query tiles.
+__device__ __forceinline__ void values_fetch(const MLA_LDS uint8_t* tile, int lane, int ch,
+                                             bf16x4 (&vb)[kOHalf][2]) {
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+  const MLA_LDS uint8_t* vbase = tile + (4 * g + (i16 >> 2)) * kLdsPitch + 4 * (i16 & 3) * 2 + 512 * ch;
+#pragma unroll
+  for (int ct = 0; ct < kOHalf; ++ct) {
+    vb[ct][0] = lds_tr16(vbase + 32 * ct);
+    vb[ct][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * ct);
+  }
+}
+
+__device__ __forceinline__ void values_mfma(const bf16x4 (&vb)[kOHalf][2], bf16x8 p0, bf16x8 p1,
+                                            f32x4 (&o0)[kOHalf], f32x4 (&o1)[kOHalf]) {
+#pragma unroll
+  for (int ct = 0; ct < kOHalf; ++ct) {
+    const bf16x4 v0 = vb[ct][0], v1 = vb[ct][1];
+    bf16x8 va;
+    va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
+    va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
+    o0[ct] = mfma16x16x32(va, p0, o0[ct]);
+    o1[ct] = mfma16x16x32(va, p1, o1[ct]);
+  }
+}
+
+// K prefetch distance (k-steps) of the score waves: the first reads go out
+// before the softmax, which covers their latency.
+constexpr int kKAhead = 6;
+
+// A query row of a work tile: row r of the tile is head r % heads of token
+// j0 + r / heads.
+struct QRow {
+  bool ok;       // the row exists
+  int qrow;      // its index in [total_q * heads]
+  int vis_last;  // last cache row its token sees
+};
+
+__device__ __forceinline__ QRow qrow_of(const PrefillArgs& a, const WorkTile& wt, int r, int block_rows) {
+  QRow x;
+  const int tok = r / a.heads;
+  const int head = r - tok * a.heads;
+  const int j = wt.j0 + tok;
+  x.ok = r < block_rows && j < wt.j1;
+  x.qrow = (wt.q0 + j) * a.heads + head;
+  x.vis_last = wt.P_b + j;
+  return x;
+}
+
+struct WsLds {
+  MLA_LDS uint8_t* ring;
+  MLA_LDS float* mx;     // [4 score waves][2 query tiles][64]: row maxes, then row sums
+  MLA_LDS uint8_t* pb;   // [2 row groups][2 query tiles][64] x 16 B probability fragments
+  MLA_LDS float* al;     // [2 row groups][2 query tiles][64]: rescale factors, then 1 / row sum
+  int* pid;              // page ids of the window
+};
+
+// One work tile, as a score wave (SCORE) or a value wave.  Both kinds pass
+// the same barriers in the same order; each keeps only its own state live.
+template <bool SCORE>
+__device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTile& wt, const WsLds& L, int w,
+                                             int lane, int block_rows) {
+  const int rg = (w & 3) >> 1;  // row group
+  const int hh = w & 1;         // score waves: tile-row half kh; value waves: column half ch
+  const int g = lane >> 4;
+  const int r0 = kBlockRows * wt.rb + 32 * rg + (lane & 15);
+  const QRow x0 = qrow_of(a, wt, r0, block_rows), x1 = qrow_of(a, wt, r0 + 16, block_rows);
+  auto stage = [&](int k) { return L.ring + (k % kPFStages) * kStageBytes; };
+  MLA_LDS float* const mx_mine = L.mx + 128 * w + lane;
+  const MLA_LDS float* const mx_part = L.mx + 128 * (w ^ 1) + lane;
+  MLA_LDS uint8_t* const pb_row = L.pb + (128 * rg + lane) * 16;  // query tile j: + 64 * 16 * j
+  MLA_LDS float* const al_row = L.al + 128 * rg + lane;           // query tile j: + 64 * j
+
+  // score-wave state
+  bf16x8 q0[kQFrags], q1[kQFrags];
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f, mx0 = -INFINITY, mx1 = -INFINITY;
+  f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
+  // value-wave state
+  f32x4 o0[kOHalf], o1[kOHalf];
+  bf16x4 vb[kOHalf][2];
+  if (SCORE) {
+    issue_q(x0.ok ? a.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
+    issue_q(x1.ok ? a.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kOHalf; ++i) o0[i] = o1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // score waves, step k: softmax of the previous tile, then the scores of tile k (kk < 0: none)
+  // (the softmax and the scores are one branch-free block)
+  auto score_step = [&](auto with_scores, int kk, int lim0, int lim1) {
+    constexpr bool kScores = decltype(with_scores)::value;
+    const MLA_LDS uint8_t* kbase = stage(kk < 0 ? 0 : kk) + tile_off(16 * hh + (lane & 15), g);
+    bf16x8 kb[kKAhead];
+    if constexpr (kScores) {
+#pragma unroll
+      for (int d = 0; d < kKAhead; ++d) kb[d] = lds_b128(kbase + 64 * d);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the first K reads go out before the softmax
+    float al0, al1;
+    const bf16x4 p0 = softmax_half(sp0, fmaxf(mx0, mx_part[0]), m0, l0, al0);
+    const bf16x4 p1 = softmax_half(sp1, fmaxf(mx1, mx_part[64]), m1, l1, al1);
+    *reinterpret_cast<MLA_LDS bf16x4*>(pb_row + 8 * hh) = p0;
+    *reinterpret_cast<MLA_LDS bf16x4*>(pb_row + 64 * 16 + 8 * hh) = p1;
+    al_row[0] = al0;  // the same factors from both partner waves
+    al_row[64] = al1;
+    if constexpr (kScores) {
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
+#pragma unroll
+      for (int ks = 0; ks < kQFrags; ++ks) {
+        const bf16x8 kf = kb[ks % kKAhead];
+        if (ks + kKAhead < kQFrags) kb[ks % kKAhead] = lds_b128(kbase + 64 * (ks + kKAhead));
+        if (ks & 1) {
+          a1 = mfma16x16x32(kf, q0[ks], a1);
+          b1 = mfma16x16x32(kf, q1[ks], b1);
+        } else {
+          a0 = mfma16x16x32(kf, q0[ks], a0);
+          b0 = mfma16x16x32(kf, q1[ks], b0);
+        }
+      }
+      mx0 = mask_half(a0 + a1, hh, lim0, a.scale_log2, lane, sp0);
+      mx1 = mask_half(b0 + b1, hh, lim1, a.scale_log2, lane, sp1);
+    }
+  };
+  // value waves: the value product of the fetched tile from the published probabilities
+  auto value_step = [&]() {
+    const bf16x8 p0 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row);
+    const bf16x8 p1 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row + 64 * 16);
+    const float al0 = al_row[0], al1 = al_row[64];
+    if (__ballot(al0 != 1.f || al1 != 1.f)) {
+#pragma unroll
+      for (int ct = 0; ct < kOHalf; ++ct) {
+        o0[ct] *= al0;
+        o1[ct] *= al1;
+      }
+    }
+    values_mfma(vb, p0, p1, o0, o1);
+  };
+
+  for (int plo = 0; plo < wt.npages; plo += kPWin) {
+    const int n = min(kPWin, wt.npages - plo);
+    lds_barrier();  // the previous window's list and stages are no longer read
+    for (int k = threadIdx.x; k < n; k += kWaves * 64)
+      L.pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
+    __builtin_amdgcn_s_waitcnt(0);  // the page ids are in LDS (and every earlier load has landed)
+    lds_barrier();
+    const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
+    auto issue = [&](int k) {
+      const int p = k >> 1;
+      stage_tile<kWaves>(a.kv + (size_t)L.pid[p] * kPageBytes, k & 1, wt.kv_end - kPage * (plo + p), stage(k), w,
+                         lane);
+    };
+    auto lim_of = [&](const QRow& x, int k) { return x.ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
+    auto wait_for = [&](int k) {  // tile k landed; tile k + 1 may stay in flight
+      if (k + 1 < ntiles) wait_tile<kWaves>(1, w); else wait_vmcnt<0>();
+    };
+    issue(0);
+    if (1 < ntiles) issue(1);
+    // step 0: scores only
+    wait_for(0);
+    lds_write_barrier();  // B1(0)
+    if (2 < ntiles) issue(2);
+    if (SCORE) {
+      f32x4 c0, c1;
+      scores_2q(stage(0), q0, q1, lane, hh, c0, c1);
+      mx0 = mask_half(c0, hh, lim_of(x0, 0), a.scale_log2, lane, sp0);
+      mx1 = mask_half(c1, hh, lim_of(x1, 0), a.scale_log2, lane, sp1);
+    }
+    lds_write_barrier();  // B2(0)
+    if (SCORE) {
+      mx_mine[0] = mx0;
+      mx_mine[64] = mx1;
+    }
+    for (int k = 1; k < ntiles; ++k) {
+      wait_for(k);
+      lds_write_barrier();  // B1(k)
+      if (k + 2 < ntiles) issue(k + 2);
+      if (SCORE)
+        score_step(std::true_type{}, k, lim_of(x0, k), lim_of(x1, k));
+      else
+        values_fetch(stage(k - 1), lane, hh, vb);
+      // B2(k): the probabilities and factors are written; the value waves'
+      // V reads may stay in flight
+      if (SCORE)
+        lds_write_barrier();
+      else
+        lds_barrier();
+      if (SCORE) {
+        mx_mine[0] = mx0;
+        mx_mine[64] = mx1;
+      } else {
+        value_step();
+      }
+    }
+    // the window's last tile
+    lds_write_barrier();  // B1'
+    if (SCORE)
+      score_step(std::false_type{}, -1, 0, 0);
+    else
+      values_fetch(stage(ntiles - 1), lane, hh, vb);
+    if (SCORE)  // B2'
+      lds_write_barrier();
+    else
+      lds_barrier();
+    if (!SCORE) value_step();
+  }
+
+  // row totals: each score wave holds the sums of its own tile rows
+  lds_write_barrier();  // the last value product is done with the probabilities and factors
+  float s0 = 0.f, s1 = 0.f;
+  if (SCORE) {
+    wait_vmcnt<0>();  // query loads of a tile that saw no cache rows
+    s0 = wave_sum_rows(l0);
+    s1 = wave_sum_rows(l1);
+    mx_mine[0] = s0;
+    mx_mine[64] = s1;
+  }
+  lds_write_barrier();
+  if (SCORE) {
+    const float t0 = s0 + mx_part[0], t1 = s1 + mx_part[64];  // the same sums in both partners
+    if (hh == 0) {
+      al_row[0] = t0 > 0.f ? 1.0f / t0 : 0.f;
+      al_row[64] = t1 > 0.f ? 1.0f / t1 : 0.f;
+      if (g == 0) {
+        if (x0.ok) a.lse[x0.qrow] = t0 > 0.f ? (m0 + fast_log2(t0)) * kLn2 : -INFINITY;
+        if (x1.ok) a.lse[x1.qrow] = t1 > 0.f ? (m1 + fast_log2(t1)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+  lds_write_barrier();
+  if (!SCORE) {
+    const float inv0 = al_row[0], inv1 = al_row[64];
+    const int col = (kDv / 2) * hh + 4 * g;
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+      const QRow& x = jq == 0 ? x0 : x1;
+      if (x.ok) {
+        uint16_t* dst = a.out + (size_t)x.qrow * kDv + col;
+#pragma unroll
+        for (int ct = 0; ct < kOHalf; ++ct) {
+          const f32x4 v = (jq == 0 ? o0[ct] : o1[ct]) * (jq == 0 ? inv0 : inv1);
+          bf16x4 h;
+          h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+          *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[kPFStages * kStageBytes];
-  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[kWaves * 64];
-  MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
-  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
+  __shared__ __attribute__((aligned(16))) float mx_raw[4 * 2 * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t pb_raw[2 * 2 * 64 * 16];
+  __shared__ __attribute__((aligned(16))) float al_raw[2 * 2 * 64];
   __shared__ int s_pid[kPWin];
   __shared__ int s_tile;
-
+  const WsLds L{(MLA_LDS uint8_t*)ring_raw, (MLA_LDS float*)mx_raw, (MLA_LDS uint8_t*)pb_raw,
+                (MLA_LDS float*)al_raw, s_pid};
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int half = w >> 2;
   const int total_tiles = a.tile_cum[a.batch];
   const int block_rows = a.tok_per_tile * a.heads;
   const int row_blocks = (block_rows + kBlockRows - 1) / kBlockRows;
-  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
-  const MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
-  auto stage = [&](int k) { return ring + (k % kPFStages) * kStageBytes; };
-
-  RowState st;
-  bf16x8 qf[kQFrags];
-
   for (;;) {
     __syncthreads();  // previous tile fully done (stages, page list, s_tile)
     if (threadIdx.x == 0) s_tile = atomicAdd(a.counter, 1);
@@ -264,68 +601,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_bf16(Prefil
     const int t = s_tile;
     if (t >= total_tiles) break;
     const WorkTile wt = locate_work(a, t, row_blocks);
-    const WaveRows x = wave_rows_of(a, wt, w, lane, block_rows);
-    if (x.wave_rows) {
-      issue_q(x.row_ok ? a.q + (size_t)x.qrow * kDqk : nullptr, lane, qf);
-      reset_state(st);
-    }
-
-    for (int plo = 0; plo < wt.npages; plo += kPWin) {
-      const int n = min(kPWin, wt.npages - plo);
-      __syncthreads();  // the previous window's list and stages are no longer read
-      for (int k = threadIdx.x; k < n; k += kWaves * 64)
-        s_pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
-      __syncthreads();
-      const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
-      auto issue = [&](int k) {
-        const int p = k >> 1;
-        stage_tile<kWaves>(a.kv + (size_t)s_pid[p] * kPageBytes, k & 1, wt.kv_end - kPage * (plo + p), stage(k),
-                           w, lane);
-      };
-      auto lim_of = [&](int k) { return x.row_ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
-      auto wait_for = [&](int k) {  // tile k landed; tile k + 1 may stay in flight
-        if (k + 1 < ntiles) wait_tile<kWaves>(1, w); else wait_vmcnt<0>();
-      };
-      issue(0);
-      if (1 < ntiles) issue(1);
-      // first step: scores only (its wait also covers the query loads)
-      wait_for(0);
-      lds_write_barrier();
-      if (2 < ntiles) issue(2);
-      f32x4 s_prev = {0.f, 0.f, 0.f, 0.f};
-      if (x.wave_rows) s_prev = tile_scores(stage(0), qf, lane, half);
-      int prev_lim = lim_of(0);
-      for (int k = 1; k < ntiles; ++k) {
-        if (x.wave_rows) *xmine = s_prev;  // scores of tile k - 1
-        wait_for(k);
-        lds_write_barrier();
-        if (k + 2 < ntiles) issue(k + 2);
-        if (x.wave_rows) {
-          const f32x4 other = *xpart;
-          const f32x4 lo = half == 0 ? s_prev : other;
-          const f32x4 hi = half == 0 ? other : s_prev;
-          s_prev = tile_step(stage(k), stage(k - 1), qf, lo, hi, prev_lim, a.scale_log2, lane, half, st);
-        }
-        prev_lim = lim_of(k);
-        lds_write_barrier();  // every wave has read its partner's slot of tile k - 1
-      }
-      // last tile of the window
-      if (x.wave_rows) *xmine = s_prev;
-      lds_write_barrier();
-      if (x.wave_rows) {
-        const f32x4 other = *xpart;
-        const f32x4 lo = half == 0 ? s_prev : other;
-        const f32x4 hi = half == 0 ? other : s_prev;
-        float alpha;
-        const bf16x8 pb = tile_softmax(lo, hi, prev_lim, a.scale_log2, lane, st, alpha);
-        rescale_o(st, alpha);
-        tile_values(stage(ntiles - 1), pb, lane, half, st);
-      }
-    }
-    if (x.wave_rows) {
-      wait_vmcnt<0>();  // query loads of a tile that saw no cache rows
-      store_rows(a, st, x, half, lane);
-    }
+    if (w < 4)
+      ws_work_tile<true>(a, wt, L, w, lane, block_rows);
+    else
+      ws_work_tile<false>(a, wt, L, w, lane, block_rows);
   }
 }
 
@@ -338,7 +617,7 @@ hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int 
   else if (kv_dtype == 2)
     hipLaunchKernelGGL(prefill_persistent_codes<kCodeFp8>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   else
-    hipLaunchKernelGGL(prefill_persistent_bf16, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL(prefill_persistent_ws, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();
 }
 
