@@ -20,6 +20,11 @@ The append leg times ``mla_kv_append`` writing that prefill workload's 8,629
 new rows into a bf16 and an INT8 cache (bytes: rows read plus rows and scales
 written); at ~20 MB per call it is partly launch-bound.
 
+The absorption leg times ``mla_q_absorb`` and ``mla_v_up`` on 8,629 tokens x
+16 heads and reports both rooflines: they are memory-bound (85 flop per
+byte), so GB/s of algorithmic bytes (inputs and weights read once, outputs
+written once) against HBM is the one that bounds them.
+
 The CPU baseline is the fp64 oracle on the host's cores (at most 16
 threads), timed on the full decode workload (all 16 query tokens, all
 heads), repeated until about 10 s of CPU work have run; it is a reported
@@ -337,15 +342,22 @@ def main() -> int:
         ao = torch.randn((AT, AH, 512), generator=g, device="cuda").to(torch.bfloat16)
         vout = torch.empty((AT, AH, 128), dtype=torch.bfloat16, device="cuda")
         legs = {}
-        for name, fn in (("q_absorb", lambda: mla.mla_q_absorb(aq, wuk, aout, AT, AH, stream)),
-                         ("v_up", lambda: mla.mla_v_up(ao, wuv, vout, AT, AH, stream))):
+        # algorithmic bytes: inputs read once, outputs written once, the weights once
+        w_bytes = AH * 512 * 128 * 2
+        for name, fn, nbytes in (
+                ("q_absorb", lambda: mla.mla_q_absorb(aq, wuk, aout, AT, AH, stream),
+                 AT * AH * (192 + 576) * 2 + w_bytes),
+                ("v_up", lambda: mla.mla_v_up(ao, wuv, vout, AT, AH, stream),
+                 AT * AH * (512 + 128) * 2 + w_bytes)):
             n = 200
             ms = time_calls([fn], stream, 2000, n) / n
             fl = 2 * AT * AH * 128 * 512
-            legs[name] = {"us_per_call": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            legs[name] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "bytes_per_call": nbytes, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                           "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "flops_per_call": fl}
         result["absorb"] = {"workload": f"{AT} tokens x {AH} heads (the prefill workload's new tokens)",
-                            "kernel": "nt_gemm (bf16 MFMA)", "bound": "mfma", **legs}
+                            "kernel": "nt_gemm (bf16 MFMA)", "bound": "hbm (85 flop/B)", **legs}
         del aq, wuk, wuv, aout, ao, vout
         torch.cuda.empty_cache()
 

@@ -11,97 +11,132 @@
 // Both are C[m][n] = sum_k A[m][k] Bt[n][k] per head ("NT"): A's rows are the
 // tokens' per-head vectors, Bt's rows the weight's output index, both
 // contiguous in k.  The caller passes W_UK[h] transposed ([512][128]) for that
-// reason; W_UV[h] ([128][512]) already is.  A workgroup computes a 64 x 64
-// tile of C with four waves of 32 x 32 (2 x 2 v_mfma_f32_16x16x32_bf16
-// blocks), operands loaded straight from global memory (16 bytes per lane,
-// the weights stay in L2 across token tiles) one k-step ahead.  The product
-// is taken transposed (D = Bt A^T) so that each lane holds four consecutive
-// output columns of one token and stores them as one 8-byte write.  fp32
+// reason; W_UV[h] ([128][512]) already is.  The work is memory-bound (85 flop
+// per byte at the absorption's shape), so the kernel is shaped around the
+// bytes: a workgroup owns 64 tokens of one head and all N output columns, so
+// each A row is read once per head; the four waves split the columns (each
+// wave: 4 token tiles x N/64 column tiles of v_mfma_f32_16x16x32_bf16, one A
+// fragment reused across the column tiles); operands come straight from
+// global memory (16 bytes per lane; the weights stay in L2 across token
+// tiles) DEPTH k-steps ahead.  The product is taken transposed (D = Bt A^T,
+// each lane holds four consecutive output columns of one token); the tile
+// goes through LDS so that the stores write whole 128-byte lines.  fp32
 // accumulation, bf16 output rounded to nearest even.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 
-constexpr int kGemmTile = 64;
+constexpr int kGemmRows = 64;  // tokens per workgroup
 
-__global__ __launch_bounds__(256) void nt_gemm(GemmArgs g) {
+// A_LDS: the 64 x K A tile is staged once in LDS with whole-row
+// direct-to-LDS loads (row r's 16-byte chunk c in slot K/8 r + (c ^ (r & 15)),
+// so the 16 rows of a fragment read fall on distinct bank groups) instead of
+// every wave loading all of it from memory; the output tile reuses that LDS.
+template <int N, int K, int DEPTH, bool A_LDS>
+__global__ __launch_bounds__(256, 2) void nt_gemm(GemmArgs g) {
+  constexpr int NW = N / 4;         // output columns per wave
+  constexpr int NT = NW / 16;       // column tiles per wave
+  constexpr int KS = K / 32;        // k-steps
+  constexpr int PITCH = 2 * N + 16; // bytes per row of the staged output tile
+  constexpr int CPR = K / 8;        // 16-byte chunks per A row
+  constexpr int OUT_BYTES = kGemmRows * PITCH;
+  constexpr int A_BYTES = A_LDS ? kGemmRows * K * 2 : 0;
+  static_assert(NT >= 1 && KS >= DEPTH && DEPTH >= 1, "shape");
+  static_assert(!A_LDS || CPR == 64, "A staging: one 1 KB row per wave load");
+  __shared__ __attribute__((aligned(1024))) uint8_t tile[OUT_BYTES > A_BYTES ? OUT_BYTES : A_BYTES];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int i16 = lane & 15, gq = lane >> 4;
-  const size_t h = blockIdx.z;
-  const int m0 = blockIdx.x * kGemmTile + 32 * (w & 1);
-  const int n0 = blockIdx.y * kGemmTile + 32 * (w >> 1);
+  const size_t h = blockIdx.y;
+  const int m0 = blockIdx.x * kGemmRows;
   const uint16_t* A = g.a + h * g.a_head;
   const uint16_t* B = g.bt + h * g.b_head;
 
-  const uint16_t* arow[2];
-  bool aok[2];
+  const uint16_t* arow[4];
+  bool aok[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int r = m0 + 16 * i + i16;
     aok[i] = r < g.m;
     arow[i] = A + (size_t)(aok[i] ? r : 0) * g.a_row + 8 * gq;
   }
-  const uint16_t* brow[2];
+  if (A_LDS) {
+    // rows past the last token repeat it (read, never used: their outputs are not stored)
+    const int last = g.m - 1 - m0;
+    MLA_LDS uint8_t* const dst = (MLA_LDS uint8_t*)tile;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) brow[j] = B + (size_t)(n0 + 16 * j + i16) * g.b_row + 8 * gq;
-
-  auto load = [](const uint16_t* p, bool ok) {
-    return ok ? *reinterpret_cast<const bf16x8*>(p) : bf16x8{};
+    for (int r = w; r < kGemmRows; r += 4) {  // wave load r: row r, lane l: chunk l ^ (r & 15)
+      const uint16_t* src = A + (size_t)(m0 + (r < last ? r : last)) * g.a_row;
+      lds_dma16(reinterpret_cast<const uint8_t*>(src), 16 * (lane ^ (r & 15)), dst + r * 1024);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  auto a_frag = [&](int i, int ks) {  // rows 16 i + i16, features 32 ks + 8 gq .. + 7
+    if (A_LDS) {
+      const int r = 16 * i + i16;
+      return *reinterpret_cast<const MLA_LDS bf16x8*>((const MLA_LDS uint8_t*)tile +
+                                                       16 * (CPR * r + ((4 * ks + gq) ^ (r & 15))));
+    }
+    return aok[i] ? *reinterpret_cast<const bf16x8*>(arow[i] + 32 * ks) : bf16x8{};
   };
-  bf16x8 ac[2], bc[2];
+  const uint16_t* brow[NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) ac[i] = load(arow[i], aok[i]);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) bc[j] = load(brow[j], true);
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NT; ++j) brow[j] = B + (size_t)(NW * w + 16 * j + i16) * g.b_row + 8 * gq;
 
-  for (int k0 = 0; k0 < g.k; k0 += 32) {
-    bf16x8 an[2], bn[2];
-    const bool more = k0 + 32 < g.k;
-    if (more) {
+  bf16x8 ac[DEPTH][4], bc[DEPTH][NT];
+  auto load = [&](int ks, int slot) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) an[i] = load(arow[i] + k0 + 32, aok[i]);
+    for (int i = 0; i < 4; ++i) ac[slot][i] = a_frag(i, ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bn[j] = load(brow[j] + k0 + 32, true);
-    }
+    for (int j = 0; j < NT; ++j) bc[slot][j] = *reinterpret_cast<const bf16x8*>(brow[j] + 32 * ks);
+  };
+  f32x4 acc[NT][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) acc[j][i] = mfma16x16x32(bc[j], ac[i], acc[j][i]);
-    if (more) {
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 2; ++i) ac[i] = an[i];
+  for (int d = 0; d < DEPTH; ++d) load(d, d);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bc[j] = bn[j];
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    const int slot = ks % DEPTH;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma16x16x32(bc[slot][j], ac[slot][i], acc[j][i]);
+    if (ks + DEPTH < KS) load(ks + DEPTH, slot);
   }
 
-  // lane holds C[m0 + 16 i + i16][n0 + 16 j + 4 gq + e], e = 0..3
-  uint16_t* C = g.c + h * g.c_head;
+  if (A_LDS) __syncthreads();  // every wave is done with the staged A tile
+  // lane holds C[16 i + i16][NW w + 16 j + 4 gq + e], e = 0..3
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (!aok[i]) continue;
-    uint16_t* crow = C + (size_t)(m0 + 16 * i + i16) * g.c_row + n0 + 4 * gq;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NT; ++j) {
       bf16x4 o;
       o[0] = (__bf16)acc[j][i][0]; o[1] = (__bf16)acc[j][i][1];
       o[2] = (__bf16)acc[j][i][2]; o[3] = (__bf16)acc[j][i][3];
-      *reinterpret_cast<bf16x4*>(crow + 16 * j) = o;
+      *reinterpret_cast<bf16x4*>(tile + (16 * i + i16) * PITCH + 2 * (NW * w + 16 * j + 4 * gq)) = o;
     }
+  __syncthreads();
+  // whole rows: N / 8 chunks of 16 bytes per token
+  uint16_t* C = g.c + h * g.c_head;
+  constexpr int OCPR = N / 8;
+#pragma unroll
+  for (int c = threadIdx.x; c < kGemmRows * OCPR; c += 256) {
+    const int r = c / OCPR, q = c - r * OCPR;
+    if (m0 + r < g.m)
+      *reinterpret_cast<u32x4*>(C + (size_t)(m0 + r) * g.c_row + 8 * q) =
+          *reinterpret_cast<const u32x4*>(tile + r * PITCH + 16 * q);
   }
 
   // absorption: the rope columns of this tile's tokens pass through unchanged
-  if (g.rope_cols > 0 && blockIdx.y == 0) {
+  if (g.rope_cols > 0) {
     const int chunks = g.rope_cols / 8;
-    for (int c = threadIdx.x; c < kGemmTile * chunks; c += 256) {
-      const int r = blockIdx.x * kGemmTile + c / chunks;
+    for (int c = threadIdx.x; c < kGemmRows * chunks; c += 256) {
+      const int r = m0 + c / chunks;
       if (r >= g.m) continue;
       const int q = c - (c / chunks) * chunks;
       *reinterpret_cast<u32x4*>(g.rope_dst + h * g.rope_dst_head + (size_t)r * g.rope_dst_row + 8 * q) =
@@ -112,8 +147,13 @@ __global__ __launch_bounds__(256) void nt_gemm(GemmArgs g) {
 
 hipError_t launch_gemm(const GemmArgs& g, int heads, hipStream_t stream) {
   if (g.m <= 0) return hipSuccess;
-  const dim3 grid((g.m + kGemmTile - 1) / kGemmTile, g.n / kGemmTile, heads);
-  hipLaunchKernelGGL(nt_gemm, grid, dim3(256), 0, stream, g);
+  const dim3 grid((g.m + kGemmRows - 1) / kGemmRows, heads);
+  if (g.n == 512 && g.k == 128)
+    hipLaunchKernelGGL((nt_gemm<512, 128, 2, false>), grid, dim3(256), 0, stream, g);
+  else if (g.n == 128 && g.k == 512)
+    hipLaunchKernelGGL((nt_gemm<128, 512, 4, true>), grid, dim3(256), 0, stream, g);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

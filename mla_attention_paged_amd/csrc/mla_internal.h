@@ -86,7 +86,7 @@ struct GemmArgs {
   size_t b_row, b_head;
   uint16_t* c;
   size_t c_row, c_head;
-  int m, n, k;                // n: a multiple of 64; k: a multiple of 32
+  int m, n, k;                // (n, k): (512, 128) or (128, 512)
   const uint16_t* rope_src;
   size_t rope_src_row, rope_src_head;
   uint16_t* rope_dst;
