@@ -34,7 +34,7 @@ def _absorb_gpu(q_bits, w_uk_bits):
     return out
 
 
-@pytest.mark.parametrize("T,H", [(1, 16), (16, 16), (65, 16), (130, 128), (3000, 16)])
+@pytest.mark.parametrize("T,H", [(1, 16), (16, 16), (64, 1), (65, 16), (129, 3), (130, 128), (3000, 16)])
 def test_q_absorb_matches_oracle(T, H):
     rng = np.random.default_rng(800 + T)
     q = _bits(rng.standard_normal((T, H, D_NOPE + D_ROPE)))
@@ -47,7 +47,7 @@ def test_q_absorb_matches_oracle(T, H):
     assert np.array_equal(got[..., D_LAT:], ref[..., D_LAT:])            # the rope passes bit for bit
 
 
-@pytest.mark.parametrize("T,H", [(1, 16), (16, 16), (65, 16), (130, 128), (3000, 16)])
+@pytest.mark.parametrize("T,H", [(1, 16), (16, 16), (64, 1), (65, 16), (129, 3), (130, 128), (3000, 16)])
 def test_v_up_matches_oracle(T, H):
     rng = np.random.default_rng(900 + T)
     o = _bits(rng.standard_normal((T, H, D_LAT)))
