@@ -28,7 +28,14 @@ written once) against HBM is the one that bounds them.
 The CPU baseline is the fp64 oracle on the host's cores (at most 16
 threads), timed on the full decode workload (all 16 query tokens, all
 heads), repeated until about 10 s of CPU work have run; it is a reported
-baseline, not a target.
+baseline, not a target.  The prefill leg carries its own: the oracle on
+128 seeded new tokens (all heads), in TFLOP/s of those tokens' flops.
+
+Besides the headline means (events around the whole timed region), the
+decode and prefill legs report per-call p10 / p50 / p90 from events around
+each call (100 and 20 calls; the events add about 2 us per call), and the
+JSON records rocm-smi's sclk / mclk before the GPU is touched and after the
+run.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
                        [--no-cpu-baseline] [--prefill-steps P] [--calib-copy-mb M]
@@ -93,6 +100,39 @@ def prefill_algorithmic_bytes(case) -> int:
     L = c.kv_lens.astype(np.int64)
     T, H = case.total_q(), case.heads
     return int(L.sum() * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4)
+
+
+def time_each(fn_list, stream, n: int) -> dict:
+    """Per-call spread: HIP events on `stream` between consecutive calls (fn_list[i % len]),
+    n calls; p10 / p50 / p90 microseconds.  The events add a little to each call; the
+    headline figures come from time_calls (no events between calls)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            ev[i].record(stream)
+            fn_list[i % len(fn_list)]()
+        ev[n].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"p10": round(float(p10), 2), "p50": round(float(p50), 2), "p90": round(float(p90), 2), "n": n}
+
+
+def gpu_clocks():
+    """sclk / mclk of the cards as rocm-smi reports them (None when it is not available)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30,
+                           close_fds=True)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    out = {}
+    for card, v in d.items():
+        if isinstance(v, dict):
+            out[card] = {k: x for k, x in v.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+    return out or None
 
 
 def time_calls(fn_list, stream, warmup: int, steps: int) -> float:
@@ -233,6 +273,7 @@ def main() -> int:
               "(see DESIGN.md for how the decode would shard). Run with --gpus 1.", file=sys.stderr)
         return 2
 
+    clocks_before = gpu_clocks()  # before this process touches the GPU
     import torch
 
     import mla_attention_paged_amd as mla
@@ -268,6 +309,7 @@ def main() -> int:
     calls = [make_call(kv) for kv in kv_copies]
     total_ms = time_calls(calls, stream, args.warmup, args.steps)
     ms_per_step = total_ms / args.steps
+    per_call = time_each(calls, stream, 100)
     nbytes = decode_algorithmic_bytes(case)
     flops = decode_flops(case)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -297,6 +339,7 @@ def main() -> int:
                      "algorithmic_bytes_per_call": nbytes,
                      "us_per_call": round(ms_per_step * 1e3, 2)},
         "decode_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "per_call_us": per_call,
         "input_generation_s": round(gen_s, 1),
     }
 
@@ -321,6 +364,7 @@ def main() -> int:
         pflops = prefill_flops(pcase)
         pms = ptotal / args.prefill_steps
         tflops = pflops / (pms * 1e-3) / 1e12
+        p_per_call = time_each([pcall], stream, 20)
         result["prefill"] = {
             "workload": pcase.name, "total_new_tokens": PT, "heads": pcase.heads,
             "prefix_lens": pcase.prefix_lens.tolist(),
@@ -329,7 +373,25 @@ def main() -> int:
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
+            "per_call_ms": {k: (round(v / 1e3, 3) if k != "n" else v) for k, v in p_per_call.items()},
         }
+        if not args.no_cpu_baseline:
+            # the oracle on a seeded sample of the new tokens (all heads), per flop
+            import oracle
+            cores = max(1, min(16, os.cpu_count() or 1))
+            sample = np.sort(np.random.default_rng(5).choice(PT, 128, replace=False)).astype(np.int32)
+            cu = pcase.cu_seqlens_q
+            req = np.searchsorted(cu, sample, side="right") - 1
+            vis = pcase.prefix_lens[req] + (sample - cu[req]) + 1
+            sflops = int(np.sum(vis.astype(np.int64)) * pcase.heads * 2 * 1088)
+            t = time.time()
+            oracle.prefill(pcase, tokens=sample, nthreads=cores)
+            cs = time.time() - t
+            result["prefill"]["cpu_baseline"] = {
+                "value": round(sflops / cs / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "seconds": round(cs, 2),
+                "sample": f"128 seeded new tokens of {PT} (all {pcase.heads} heads), fp64 C oracle; "
+                          f"{sflops} flops of the call's {pflops}"}
 
     # ---------------- absorption and up-projection on the prefill workload's tokens ----------------
     if not args.no_absorb:
@@ -514,6 +576,7 @@ def main() -> int:
                                   "kind": "oracle", "seconds": round(cpu_s, 2), "runs": runs,
                                   "sample": f"the full {case.name} call (all {T} query tokens x {H} heads), "
                                             f"fp64 C oracle, {runs} runs"}
+    result["gpu_clocks"] = {"before": clocks_before, "after": gpu_clocks()}
     print(json.dumps(result))
     return 0
 
