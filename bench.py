@@ -156,7 +156,7 @@ def time_calls(fn_list, stream, warmup: int, steps: int) -> float:
 
 
 # the sources that shape the decode call's kernels and plan (its recorded HBM traffic is
-# dropped when any of them changes)
+# dropped when the code of any of them changes; comments do not count)
 KERNEL_SOURCES = ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_decode.hip",
                   "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h"]
 COUNTER_RUN_FLAGS = ("--steps 5 --warmup 20 --no-prefill --no-append --no-cpu-baseline --no-absorb --no-pages "
@@ -164,13 +164,40 @@ COUNTER_RUN_FLAGS = ("--steps 5 --warmup 20 --no-prefill --no-append --no-cpu-ba
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_decode_b4_h16_q4_L64K_traffic.json")
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without comments, each line's trailing blanks and blank lines:
+    the code the digest covers (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = [ln.rstrip() for ln in "".join(out).split("\n")]
+    return "\n".join(ln for ln in lines if ln)
+
+
 def sources_digest() -> str:
+    """SHA-256 of the code (comments stripped) of the sources that shape the decode call."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()
+
 
 
 def recorded_traffic(workload: str):
@@ -225,6 +252,7 @@ def record_traffic(fetch_dir: str, write_dir: str, calib_mb: int) -> int:
         total += fb + wb
     import synth
     rec = {"workload": synth.make_workload(1).name, "source_sha256": sources_digest(),
+           "source_digest": "SHA-256 of the decode sources' code, comments stripped (bench.strip_comments)",
            "hbm_bytes_per_call": round(total), "per_kernel": per_kernel,
            "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
            "calibration": f"plain device copy of {calib_mb} MiB (torch copy_), largest copy dispatch reading",

@@ -1,10 +1,14 @@
 // Device building blocks shared by the decode and prefill kernels (gfx950).
 //
-// A workgroup of eight waves (two per SIMD) attends a block of up to 64
-// query rows against the cache, which it streams through a ring of four
-// LDS stages of 32 cache rows (half a page) each: three tiles are in flight
-// while the fourth is consumed.  Waves w and w + 4 share the 16 query rows
-// 16 (w % 4) .. +15 and split the work of each tile in two halves, h = w / 4:
+// A workgroup of eight waves (two per SIMD: waves w and w + 4 share one)
+// attends a block of up to 64 query rows against the cache, which it
+// streams through a ring of LDS stages of 32 cache rows (half a page) each
+// (three stages in the bf16 decode kernel, four in the bf16 prefill kernel,
+// code stages plus converted buffers in the INT8 / FP8 kernels).  In the
+// decode kernels and the INT8 / FP8 prefill kernel, waves w and w + 4 share
+// the 16 query rows 16 (w % 4) .. +15 and split the work of each tile in two
+// halves, h = w / 4 (the bf16 prefill kernel specialises its waves instead:
+// score waves and value waves on 32-row groups, in mla_prefill.hip):
 //
 //   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over the 576 features: A = 16
 //                   cache rows (rows 16h .. 16h + 15 of the tile) read from
