@@ -77,6 +77,19 @@ def test_decode_split_plans_agree(cus):
     assert_close(out, lse, ref_out, ref_lse, f"cus {cus}")
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("cus", [1, 2])
+def test_decode_multi_window_shares(cus, kv_dtype):
+    """148 pages on one or two workgroups: shares longer than the 128-page window of
+    the tile list, request switches inside a window, and (one workgroup) the final
+    output written by phase one itself."""
+    case = synth.make_decode_case(208, 4, 16, 4, seq_lens=[5000, 64, 4000, 300], kv_dtype=kv_dtype)
+    with _cus(cus):
+        out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, f"cus {cus} {kv_dtype}")
+
+
 def test_decode_workload0_full():
     case = synth.make_workload(0)
     out, lse = host(*run_decode(case))
