@@ -286,6 +286,8 @@ def main() -> int:
                     help="skip the ragged-draft decode leg (1..4 drafts per request) on the 64K decode shape")
     ap.add_argument("--no-scaled", action="store_true",
                     help="skip the INT8 / FP8 cache decode leg on the 64K decode shape")
+    ap.add_argument("--no-scaled-prefill", action="store_true",
+                    help="skip the INT8 / FP8 cache prefill leg on the prefill workload's shape")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), whose "
@@ -539,6 +541,39 @@ def main() -> int:
         result["scaled_cache_decode"] = {"workload": f"{case.name} with INT8 / FP8 (E4M3) rows and fp32 row scales",
                                          "kernel": "mla_decode call (decode_phase1<scaled> + decode_merge)",
                                          "bound": "hbm", **legs}
+
+    # ---------------- scaled caches: the prefill workload's shape with INT8 and FP8 rows ----------------
+    if not args.no_scaled_prefill and not args.no_prefill:
+        legs = {}
+        base3 = synth.make_workload(3)
+        for dt in ("int8", "fp8"):
+            qcase = synth.make_prefill_case(4, base3.heads, prefix_lens=base3.prefix_lens,
+                                            new_lens=np.diff(base3.cu_seqlens_q), kv_dtype=dt,
+                                            name=f"{base3.name}_{dt}")
+            qin = prefill_inputs(qcase)
+            QT = qcase.total_q()
+            qout = torch.empty((QT, qcase.heads, 512), dtype=torch.bfloat16, device="cuda")
+            qlse = torch.empty((QT, qcase.heads), dtype=torch.float32, device="cuda")
+            qws_b = mla.mla_splitkv_workspace_size(qcase.batch, qcase.heads, qcase.max_q_len(), QT,
+                                                   qcase.max_seq_len, qin["kind"])
+            qws = torch.empty(max(qws_b, 1), dtype=torch.uint8, device="cuda")
+
+            def qcall(qin=qin, qcase=qcase, QT=QT, qout=qout, qlse=qlse, qws=qws):
+                mla.mla_prefill_varlen(qin["q"], qin["cu"], qin["prefix"], qin["kv"], qin["scale"], qin["kind"],
+                                       qin["pt"], qcase.cache.max_pages, qcase.batch, QT, qcase.max_q_len(),
+                                       qcase.max_seq_len, qcase.heads, 64, qcase.softmax_scale, qout, qlse,
+                                       qws, qws.numel(), stream)
+
+            qms = time_calls([qcall], stream, 2, 3) / 3
+            qfl = prefill_flops(qcase)
+            legs[dt] = {"ms_per_call": round(qms, 3), "tflops": round(qfl / (qms * 1e-3) / 1e12, 1),
+                        "frac_mfma": round(qfl / (qms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            del qin, qout, qlse, qws
+            torch.cuda.empty_cache()
+        result["scaled_cache_prefill"] = {
+            "workload": f"{base3.name} with INT8 / FP8 (E4M3) rows and fp32 row scales",
+            "kernel": "mla_prefill_varlen call (prefill_persistent_ws_codes: the value waves convert the next tile's codes)",
+            "bound": "mfma", **legs}
 
     # ---------------- append leg: the prefill workload's new rows into the cache ----------------
     if not args.no_append:

@@ -5,10 +5,10 @@
 // streams through a ring of LDS stages of 32 cache rows (half a page) each
 // (three stages in the bf16 decode kernel, four in the bf16 prefill kernel,
 // code stages plus converted buffers in the INT8 / FP8 kernels).  In the
-// decode kernels and the INT8 / FP8 prefill kernel, waves w and w + 4 share
-// the 16 query rows 16 (w % 4) .. +15 and split the work of each tile in two
-// halves, h = w / 4 (the bf16 prefill kernel specialises its waves instead:
-// score waves and value waves on 32-row groups, in mla_prefill.hip):
+// decode kernels, waves w and w + 4 share the 16 query rows 16 (w % 4) ..
+// +15 and split the work of each tile in two halves, h = w / 4 (the prefill
+// kernels specialise their waves instead: score waves and value waves on
+// 32-row groups, in mla_prefill.hip):
 //
 //   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over the 576 features: A = 16
 //                   cache rows (rows 16h .. 16h + 15 of the tile) read from
@@ -67,7 +67,6 @@ constexpr int kTileSlots = kTileRows * kLdsChunks;      // 2368 16-byte slots
 constexpr int kStageLoads = kTileSlots / 64;            // 37 wave-wide loads per tile
 static_assert(kStageLoads * 64 == kTileSlots, "a tile is a whole number of wave-wide loads");
 constexpr int kStageBytes = kStageLoads * 1024;         // 37888
-constexpr int kStages = 4;                     // ring depth: 3 tiles in flight
 
 // INT8 / FP8 cache: a stage holds the 32 rows' codes (576 B each, unpadded: they
 // are only read by the conversion pass, 16 contiguous bytes per lane) and
@@ -79,16 +78,6 @@ constexpr int kI8CodeBytes = kTileRows * kI8RowBytes;      // 18432: 18 wave-wid
 constexpr int kI8CodeLoads = kI8CodeBytes / 1024;
 constexpr int kI8StageLoads = kI8CodeLoads + 1;            // + one 8-lane load of the scales
 constexpr int kI8StageBytes = kI8CodeBytes + kTileRows * 4;  // 18560
-constexpr int kI8Stages = 6;
-
-// Ring geometry of each cache type.
-template <bool I8>
-struct Ring {
-  static constexpr int loads = I8 ? kI8StageLoads : kStageLoads;
-  static constexpr int stage_bytes = I8 ? kI8StageBytes : kStageBytes;
-  static constexpr int stages = I8 ? kI8Stages : kStages;
-  static constexpr int page_bytes = I8 ? kI8PageBytes : kPageBytes;
-};
 constexpr int kQFrags = kDqk / 32;             // 18 k-steps of 32 features
 constexpr int kOFrags = kDv / 16;              // 32 value-column tiles
 constexpr int kWaves = 8;                      // waves per workgroup (two per SIMD)
@@ -277,44 +266,44 @@ __device__ __forceinline__ unsigned codepair_to_bf16(unsigned x) {
 }
 
 // Convert a staged tile's codes (INT8 or E4M3) into exact bf16 values in
-// `cvt`, laid out like a staged bf16 tile (pitch 1184), cooperatively by the
-// workgroup's kWaves * 64 threads: thread i converts 16-byte chunks i, i + 512
-// and (i < 128) i + 1024 of the 1152, all of whose loads are issued before
-// the first conversion (one LDS round trip instead of three).
-template <int CODE>
+// `cvt`, laid out like a staged bf16 tile (pitch 1184), cooperatively by
+// kThreads threads (the workgroup's, by default).  The unit is 8 codes (8
+// bytes in, 16 bytes out): thread i converts units i, i + kThreads, ... of
+// the 2304, all of whose loads are issued before the first conversion (one
+// LDS round trip), and consecutive lanes read and write consecutive slots,
+// so neither side has bank conflicts (16 codes per lane written as two
+// 16-byte halves 32 bytes apart conflicted 8 ways).
+template <int CODE, int kThreads = kWaves * 64>
 __device__ __forceinline__ void convert_code_tile(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt, int tid) {
-  constexpr int kThreads = kWaves * 64;
-  constexpr int kChunks = kI8CodeBytes / 16;
-  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
-  static_assert(kPer == 3 && kChunks > 2 * kThreads, "chunk split");
-  u32x4 x[kPer];
+  constexpr int kUnits = kI8CodeBytes / 8;  // 2304
+  constexpr int kPer = (kUnits + kThreads - 1) / kThreads;
+  constexpr int kRowUnits = kI8RowBytes / 8;  // 72
+  static_assert(kUnits > (kPer - 1) * kThreads, "only the last round of units is partial");
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t x[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (i < kPer - 1 || tid + i * kThreads < kChunks)
-      x[i] = *reinterpret_cast<const MLA_LDS u32x4*>(stage + 16 * (tid + i * kThreads));
+    if (i < kPer - 1 || tid + i * kThreads < kUnits)
+      x[i] = *reinterpret_cast<const MLA_LDS u32x2_t*>(stage + 8 * (tid + i * kThreads));
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int c = tid + i * kThreads;
-    if (i < kPer - 1 || c < kChunks) {
-      const int t = c / 36, j = c - 36 * t;
-      u32x4 lo, hi;
-      lo[0] = codepair_to_bf16<CODE, 0>(x[i][0]); lo[1] = codepair_to_bf16<CODE, 1>(x[i][0]);
-      lo[2] = codepair_to_bf16<CODE, 0>(x[i][1]); lo[3] = codepair_to_bf16<CODE, 1>(x[i][1]);
-      hi[0] = codepair_to_bf16<CODE, 0>(x[i][2]); hi[1] = codepair_to_bf16<CODE, 1>(x[i][2]);
-      hi[2] = codepair_to_bf16<CODE, 0>(x[i][3]); hi[3] = codepair_to_bf16<CODE, 1>(x[i][3]);
-      MLA_LDS u32x4* dst = reinterpret_cast<MLA_LDS u32x4*>(cvt + t * kLdsPitch + 32 * j);
-      dst[0] = lo;
-      dst[1] = hi;
+    const int u = tid + i * kThreads;
+    if (i < kPer - 1 || u < kUnits) {
+      const int t = u / kRowUnits, j = u - kRowUnits * t;
+      u32x4 o;
+      o[0] = codepair_to_bf16<CODE, 0>(x[i][0]); o[1] = codepair_to_bf16<CODE, 1>(x[i][0]);
+      o[2] = codepair_to_bf16<CODE, 0>(x[i][1]); o[3] = codepair_to_bf16<CODE, 1>(x[i][1]);
+      *reinterpret_cast<MLA_LDS u32x4*>(cvt + t * kLdsPitch + 16 * j) = o;
     }
   }
 }
 
 // The same, and the tile's 32 row scales copied to `tsc` (for the pipelined
 // core, which reads a tile's scales one step after its codes are gone).
-template <int CODE>
+template <int CODE, int kThreads = kWaves * 64>
 __device__ __forceinline__ void convert_code_tile_sc(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt,
                                                      MLA_LDS float* tsc, int tid) {
-  convert_code_tile<CODE>(stage, cvt, tid);
+  convert_code_tile<CODE, kThreads>(stage, cvt, tid);
   if (tid < kTileRows / 4)
     reinterpret_cast<MLA_LDS f32x4*>(tsc)[tid] = reinterpret_cast<const MLA_LDS f32x4*>(stage + kI8CodeBytes)[tid];
 }
@@ -415,131 +404,6 @@ __device__ __forceinline__ bf16x4 lds_tr16(const MLA_LDS uint8_t* p) {
 // LDS read prefetch distances (in MFMA steps) of the two contractions.
 constexpr int kKDepth = 3;
 constexpr int kVDepth = 3;
-
-// Attend one staged tile of 32 rows (see the top of this file).  Token tt of
-// the tile is visible to this lane's row when tt <= lim (lim >= 31: all).
-// `half` is w / 4; xmine / xpart are this wave's and its partner's 1 KB
-// exchange slots.
-// With SCALED (INT8 cache), `tile` holds the exact integer codes and `tsc`
-// the 32 rows' scales: row t's score is multiplied by tsc[t] and its
-// probability by tsc[t] before the value product (never per element); the
-// row sum uses the unscaled probabilities.
-template <bool SCALED = false>
-__device__ __forceinline__ void attend_tile(const MLA_LDS uint8_t* tile, const bf16x8 (&qf)[kQFrags],
-                                            int lim, float scale_log2, int lane, int half,
-                                            MLA_LDS f32x4* xmine, const MLA_LDS f32x4* xpart,
-                                            RowState& st, const MLA_LDS float* tsc = nullptr) {
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-
-  // ---- S^T = K Q^T for this wave's 16 rows of the tile ----
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 kb[kKDepth + 1];
-  const MLA_LDS uint8_t* kbase = tile + tile_off(16 * half + r16, g);
-#pragma unroll
-  for (int d = 0; d < kKDepth; ++d) kb[d] = lds_b128(kbase + 64 * d);
-#pragma unroll
-  for (int ks = 0; ks < kQFrags; ++ks) {
-    if (ks + kKDepth < kQFrags) kb[(ks + kKDepth) % (kKDepth + 1)] = lds_b128(kbase + 64 * (ks + kKDepth));
-    acc = mfma16x16x32(kb[ks % (kKDepth + 1)], qf[ks], acc);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // ---- swap score blocks with the partner wave ----
-  *xmine = acc;
-  lds_write_barrier();
-  const f32x4 other = *xpart;
-  const f32x4 lo = half == 0 ? acc : other;  // tile rows 4g + e
-  const f32x4 hi = half == 0 ? other : acc;  // tile rows 16 + 4g + e
-
-  // First value fragments: requested now, consumed after the softmax.
-  // Transposed reads: lane i of its 16-lane group supplies row 4g + i/4 (and
-  // that + 16) and columns 256h + 16ct + 4(i%4) .. +3, and receives the 4
-  // rows of column 256h + 16ct + i.
-  const int i16 = lane & 15;
-  const int colq = 4 * (i16 & 3);
-  const int tq = 4 * g + (i16 >> 2);
-  const MLA_LDS uint8_t* vbase = tile + tq * kLdsPitch + colq * 2 + 512 * half;
-  bf16x4 vb[kVDepth + 1][2];
-#pragma unroll
-  for (int d = 0; d < kVDepth; ++d) {
-    vb[d][0] = lds_tr16(vbase + 32 * d);
-    vb[d][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * d);
-  }
-
-  // ---- scale, mask, online softmax (bitwise identical in both waves) ----
-  f32x4 sc_lo = {1.f, 1.f, 1.f, 1.f}, sc_hi = {1.f, 1.f, 1.f, 1.f};
-  if (SCALED) {
-    sc_lo = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 4 * g);
-    sc_hi = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 16 + 4 * g);
-  }
-  float s[8];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v0 = lo[e] * scale_log2, v1 = hi[e] * scale_log2;
-    if (SCALED) {
-      v0 *= sc_lo[e];
-      v1 *= sc_hi[e];
-    }
-    v0 = 4 * g + e <= lim ? v0 : -INFINITY;
-    v1 = 16 + 4 * g + e <= lim ? v1 : -INFINITY;
-    s[e] = v0;
-    s[4 + e] = v1;
-    mx = fmaxf(mx, fmaxf(v0, v1));
-  }
-  mx = wave_max_rows(mx);
-  // Raise the max only when the tile's max exceeds it by more than the slack.
-  const bool raise = mx > st.m + kRescaleSlack;
-  if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
-    const float m_new = raise ? mx : st.m;
-    const float alpha = fast_exp2(st.m - m_new);  // st.m = -inf: 0; unchanged rows: 1
-    st.m = m_new;
-    st.l *= alpha;
-#pragma unroll
-    for (int c0 = 0; c0 < kOHalf; c0 += 4) {
-#pragma unroll
-      for (int ct = c0; ct < c0 + 4; ++ct) st.o[ct] *= alpha;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  const float m_use = st.m == -INFINITY ? 0.f : st.m;
-  float psum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    s[i] = fast_exp2(s[i] - m_use);
-    psum += s[i];
-  }
-  st.l += psum;
-  bf16x8 pb;
-  if (SCALED) {
-    // masked rows have probability 0 but possibly a non-finite scale: select, not multiply
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pb[e] = (__bf16)(4 * g + e <= lim ? s[e] * sc_lo[e] : 0.f);
-      pb[4 + e] = (__bf16)(16 + 4 * g + e <= lim ? s[4 + e] * sc_hi[e] : 0.f);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- O^T += V^T P^T: 32 rows x this wave's 16 column tiles ----
-#pragma unroll
-  for (int ct = 0; ct < kOHalf; ++ct) {
-    if (ct + kVDepth < kOHalf) {
-      vb[(ct + kVDepth) % (kVDepth + 1)][0] = lds_tr16(vbase + 32 * (ct + kVDepth));
-      vb[(ct + kVDepth) % (kVDepth + 1)][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * (ct + kVDepth));
-    }
-    const bf16x4 v0 = vb[ct % (kVDepth + 1)][0], v1 = vb[ct % (kVDepth + 1)][1];
-    bf16x8 va;
-    va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
-    va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
-    st.o[ct] = mfma16x16x32(va, pb, st.o[ct]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Pipelined core (bf16 cache).  A wave's work on a tile is split into three

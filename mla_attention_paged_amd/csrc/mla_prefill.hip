@@ -108,124 +108,6 @@ __device__ __forceinline__ WorkTile locate_work(const PrefillArgs& a, int t, int
   return w;
 }
 
-// Rows of a work tile owned by a wave of 16 rows: row r of the tile is head
-// r % heads of token j0 + r / heads.
-struct WaveRows {
-  bool wave_rows, row_ok;
-  int qrow;      // index of the lane's query row in [total_q * heads]
-  int vis_last;  // last cache row its token sees
-};
-
-__device__ __forceinline__ WaveRows wave_rows_of(const PrefillArgs& a, const WorkTile& wt, int w, int lane,
-                                                 int block_rows) {
-  WaveRows x;
-  const int r = kBlockRows * wt.rb + 16 * (w & 3) + (lane & 15);
-  x.wave_rows = kBlockRows * wt.rb + 16 * (w & 3) < block_rows;
-  const int tok_in_tile = r / a.heads;
-  const int head = r - tok_in_tile * a.heads;
-  const int j = wt.j0 + tok_in_tile;                   // this lane's new-token index
-  x.row_ok = x.wave_rows && r < block_rows && j < wt.j1;
-  x.qrow = (wt.q0 + j) * a.heads + head;
-  x.vis_last = wt.P_b + j;                             // last visible cache row of this query token
-  return x;
-}
-
-__device__ __forceinline__ void store_rows(const PrefillArgs& a, const RowState& st, const WaveRows& x, int half,
-                                           int lane) {
-  float inv, lse2;
-  finish_row(st, inv, lse2);
-  if (x.row_ok) {
-    const int g = lane >> 4;
-    uint16_t* dst = a.out + (size_t)x.qrow * kDv + (kDv / 2) * half + 4 * g;
-#pragma unroll
-    for (int ct = 0; ct < kOHalf; ++ct) {
-      const f32x4 v = st.o[ct] * inv;
-      bf16x4 h;
-      h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
-      *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
-    }
-    if (g == 0 && half == 0) a.lse[x.qrow] = lse2 * kLn2;
-  }
-}
-
-// INT8 or FP8 cache (CODE): the lockstep core.  Every tile is converted to
-// bf16 in LDS by all waves after its barrier, then scored, normalised and
-// accumulated before the next tile starts; R::stages - 1 tiles are in flight.
-template <int CODE>
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_codes(PrefillArgs a) {
-  using R = Ring<true>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[R::stages * R::stage_bytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[kStageBytes];
-  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[kWaves * 64];
-  MLA_LDS uint8_t* const ring = (MLA_LDS uint8_t*)ring_raw;
-  MLA_LDS uint8_t* const cvt = (MLA_LDS uint8_t*)cvt_raw;
-  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
-  __shared__ int s_pid[kPWin];
-  __shared__ int s_tile;
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int half = w >> 2;
-  const int total_tiles = a.tile_cum[a.batch];
-  const int block_rows = a.tok_per_tile * a.heads;                 // query rows of a token tile
-  const int row_blocks = (block_rows + kBlockRows - 1) / kBlockRows;
-  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
-  const MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
-
-  RowState st;
-  bf16x8 qf[kQFrags];
-
-  for (;;) {
-    __syncthreads();  // previous tile fully done (stages, page list, s_tile)
-    if (threadIdx.x == 0) s_tile = atomicAdd(a.counter, 1);
-    __syncthreads();
-    const int t = s_tile;
-    if (t >= total_tiles) break;
-    const WorkTile wt = locate_work(a, t, row_blocks);
-    const WaveRows x = wave_rows_of(a, wt, w, lane, block_rows);
-    if (x.wave_rows) {
-      load_q(x.row_ok ? a.q + (size_t)x.qrow * kDqk : nullptr, lane, qf);
-      reset_state(st);
-    }
-
-    for (int plo = 0; plo < wt.npages; plo += kPWin) {
-      const int n = min(kPWin, wt.npages - plo);
-      __syncthreads();
-      for (int k = threadIdx.x; k < n; k += kWaves * 64)
-        s_pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
-      __syncthreads();
-      // tiles of 32 rows: only those holding a row the tile's last token sees
-      const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
-      auto issue = [&](int k) {
-        const int p = k >> 1;
-        MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
-        const int rem = wt.kv_end - kPage * (plo + p);
-        stage_tile_i8<kWaves>(a.kv + (size_t)s_pid[p] * kI8PageBytes, a.kv_scale + (size_t)s_pid[p] * kPage,
-                              k & 1, rem, stage, w, lane);
-      };
-      const int pre = min(R::stages - 1, ntiles);
-      for (int k = 0; k < pre; ++k) issue(k);
-      for (int k = 0; k < ntiles; ++k) {
-        const int t0 = kPage * plo + kTileRows * k;  // first cache row of tile k
-        wait_tile<kWaves, R::loads>(min(R::stages - 2, ntiles - 1 - k), w);
-        lds_barrier();
-        if (k + R::stages - 1 < ntiles) issue(k + R::stages - 1);
-        const MLA_LDS uint8_t* stage = ring + (k % R::stages) * R::stage_bytes;
-        convert_code_tile<CODE>(stage, cvt, threadIdx.x);
-        lds_write_barrier();
-        if (x.wave_rows) {
-          const int lim = x.row_ok ? x.vis_last - t0 : -1;
-          attend_tile<true>(cvt, qf, lim, a.scale_log2, lane, half, xmine, xpart, st,
-                            reinterpret_cast<const MLA_LDS float*>(stage + kI8CodeBytes));
-        } else {
-          lds_write_barrier();  // the exchange barrier inside attend_tile
-        }
-      }
-    }
-    if (x.wave_rows) store_rows(a, st, x, half, lane);
-  }
-}
-
 // bf16 cache: a ring of four stages, two tiles in flight while two are read
 // (tile k by the score waves, tile k - 1 by the value waves).  A third stage
 // only, with one tile in flight, left the tile's load latency exposed in an
@@ -608,14 +490,314 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws(PrefillA
   }
 }
 
+// ---------------------------------------------------------------------------
+// INT8 / FP8 cache (CODE) on the wave-specialised core (K prefetch depth
+// kKAheadC: the score waves here also hold the row scales).  The codes stream
+// through two LDS code stages; the value waves, whose score-phase work is
+// only the fetch of a tile's V fragments, also convert the next tile's
+// codes to exact bf16 there, into the third of three converted buffers
+// (with the tile's 32 row scales beside it).  Step k:
+//  - B1(k): the codes of tile k + 1 have landed; tile k is converted;
+//  - score waves: softmax of tile k - 1 (probabilities times their row's
+//    scale, selected to 0 on masked rows so that a non-finite scale there
+//    cannot leak; the row sums take the unscaled probabilities), then the
+//    scores of tile k, each row's score times its scale;
+//  - value waves: V fragments of tile k - 1, then tile k + 1's conversion;
+//  - B2(k): tile k + 1's code stage is free: tile k + 3's codes go into it;
+//  - value waves: the value product of tile k - 1.
+// ---------------------------------------------------------------------------
+
+// mask_half with each tile row's scale (sc: rows 16kh + 4(lane>>4) + e).
+__device__ __forceinline__ float mask_half_sc(f32x4 acc, f32x4 sc, int kh, int lim, float scale_log2, int lane,
+                                              f32x4& s) {
+  const int g = lane >> 4;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = 16 * kh + 4 * g + e <= lim ? acc[e] * scale_log2 * sc[e] : -INFINITY;
+    s[e] = v;
+    mx = fmaxf(mx, v);
+  }
+  return wave_max_rows(mx);
+}
+
+// softmax_half whose published probabilities carry their row's scale.
+__device__ __forceinline__ bf16x4 softmax_half_sc(const f32x4& s, f32x4 sc, float mx, float& m, float& lh,
+                                                  float& alpha) {
+  const float m_new = mx > m + kRescaleSlack ? mx : m;
+  alpha = m_new == m ? 1.f : fast_exp2(m - m_new);
+  m = m_new;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  bf16x4 p;
+  float ps = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = fast_exp2(s[e] - m_use);
+    ps += v;
+    p[e] = (__bf16)(s[e] == -INFINITY ? 0.f : v * sc[e]);
+  }
+  lh = lh * alpha + ps;
+  return p;
+}
+
+constexpr int kKAheadC = 4;
+
+struct WsCodesLds {
+  MLA_LDS uint8_t* codes;  // two code stages
+  MLA_LDS uint8_t* cvt;    // three converted tiles (bf16, pitch 1184)
+  MLA_LDS float* tsc;      // their row scales, 32 each
+  MLA_LDS float* mx;
+  MLA_LDS uint8_t* pb;
+  MLA_LDS float* al;
+  int* pid;
+};
+
+template <bool SCORE, int CODE>
+__device__ __forceinline__ void ws_codes_work_tile(const PrefillArgs& a, const WorkTile& wt, const WsCodesLds& L,
+                                                   int w, int lane, int block_rows) {
+  const int rg = (w & 3) >> 1;
+  const int hh = w & 1;
+  const int g = lane >> 4;
+  const int r0 = kBlockRows * wt.rb + 32 * rg + (lane & 15);
+  const QRow x0 = qrow_of(a, wt, r0, block_rows), x1 = qrow_of(a, wt, r0 + 16, block_rows);
+  auto code_stage = [&](int k) { return L.codes + (k & 1) * kI8StageBytes; };
+  auto cvt_of = [&](int k) { return L.cvt + (k % 3) * kStageBytes; };
+  auto tsc4 = [&](int k) {  // this lane's four row scales of tile k (score waves: rows 16kh + 4g + e)
+    return *reinterpret_cast<const MLA_LDS f32x4*>(L.tsc + (k % 3) * kTileRows + 16 * hh + 4 * g);
+  };
+  MLA_LDS float* const mx_mine = L.mx + 128 * w + lane;
+  const MLA_LDS float* const mx_part = L.mx + 128 * (w ^ 1) + lane;
+  MLA_LDS uint8_t* const pb_row = L.pb + (128 * rg + lane) * 16;
+  MLA_LDS float* const al_row = L.al + 128 * rg + lane;
+
+  bf16x8 q0[kQFrags], q1[kQFrags];
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f, mx0 = -INFINITY, mx1 = -INFINITY;
+  f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
+  f32x4 o0[kOHalf], o1[kOHalf];
+  bf16x4 vb[kOHalf][2];
+  if (SCORE) {
+    issue_q(x0.ok ? a.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
+    issue_q(x1.ok ? a.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kOHalf; ++i) o0[i] = o1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto score_tile = [&](int kk, int lim0, int lim1) {
+    f32x4 c0, c1;
+    scores_2q(cvt_of(kk), q0, q1, lane, hh, c0, c1);
+    const f32x4 sc = tsc4(kk);
+    mx0 = mask_half_sc(c0, sc, hh, lim0, a.scale_log2, lane, sp0);
+    mx1 = mask_half_sc(c1, sc, hh, lim1, a.scale_log2, lane, sp1);
+  };
+  // score waves, step kk: softmax of tile kprev, then (with_scores) the scores of tile kk
+  auto score_step = [&](auto with_scores, int kk, int kprev, int lim0, int lim1) {
+    constexpr bool kScores = decltype(with_scores)::value;
+    const MLA_LDS uint8_t* kbase = cvt_of(kk < 0 ? 0 : kk) + tile_off(16 * hh + (lane & 15), g);
+    bf16x8 kb[kKAheadC];
+    if constexpr (kScores) {
+#pragma unroll
+      for (int d = 0; d < kKAheadC; ++d) kb[d] = lds_b128(kbase + 64 * d);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the first K reads go out before the softmax
+    const f32x4 scp = tsc4(kprev);
+    float al0, al1;
+    const bf16x4 p0 = softmax_half_sc(sp0, scp, fmaxf(mx0, mx_part[0]), m0, l0, al0);
+    const bf16x4 p1 = softmax_half_sc(sp1, scp, fmaxf(mx1, mx_part[64]), m1, l1, al1);
+    *reinterpret_cast<MLA_LDS bf16x4*>(pb_row + 8 * hh) = p0;
+    *reinterpret_cast<MLA_LDS bf16x4*>(pb_row + 64 * 16 + 8 * hh) = p1;
+    al_row[0] = al0;
+    al_row[64] = al1;
+    if constexpr (kScores) {
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
+#pragma unroll
+      for (int ks = 0; ks < kQFrags; ++ks) {
+        const bf16x8 kf = kb[ks % kKAheadC];
+        if (ks + kKAheadC < kQFrags) kb[ks % kKAheadC] = lds_b128(kbase + 64 * (ks + kKAheadC));
+        if (ks & 1) {
+          a1 = mfma16x16x32(kf, q0[ks], a1);
+          b1 = mfma16x16x32(kf, q1[ks], b1);
+        } else {
+          a0 = mfma16x16x32(kf, q0[ks], a0);
+          b0 = mfma16x16x32(kf, q1[ks], b0);
+        }
+      }
+      const f32x4 sc = tsc4(kk);
+      mx0 = mask_half_sc(a0 + a1, sc, hh, lim0, a.scale_log2, lane, sp0);
+      mx1 = mask_half_sc(b0 + b1, sc, hh, lim1, a.scale_log2, lane, sp1);
+    }
+  };
+  auto value_step = [&]() {
+    const bf16x8 p0 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row);
+    const bf16x8 p1 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row + 64 * 16);
+    const float al0 = al_row[0], al1 = al_row[64];
+    if (__ballot(al0 != 1.f || al1 != 1.f)) {
+#pragma unroll
+      for (int ct = 0; ct < kOHalf; ++ct) {
+        o0[ct] *= al0;
+        o1[ct] *= al1;
+      }
+    }
+    values_mfma(vb, p0, p1, o0, o1);
+  };
+  // value waves: convert tile kk's codes (256 threads)
+  auto convert = [&](int kk) {
+    convert_code_tile_sc<CODE, 4 * 64>(code_stage(kk), cvt_of(kk), L.tsc + (kk % 3) * kTileRows,
+                                       threadIdx.x - 4 * 64);
+  };
+
+  for (int plo = 0; plo < wt.npages; plo += kPWin) {
+    const int n = min(kPWin, wt.npages - plo);
+    lds_barrier();
+    for (int k = threadIdx.x; k < n; k += kWaves * 64)
+      L.pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
+    auto issue = [&](int k) {
+      const int p = k >> 1;
+      stage_tile_i8<kWaves>(a.kv + (size_t)L.pid[p] * kI8PageBytes, a.kv_scale + (size_t)L.pid[p] * kPage, k & 1,
+                            wt.kv_end - kPage * (plo + p), code_stage(k), w, lane);
+    };
+    auto lim_of = [&](const QRow& x, int k) { return x.ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
+    auto wait_codes = [&](int k) {  // tile k's codes landed; tile k + 1's may stay in flight
+      if (k + 1 < ntiles)
+        wait_tile<kWaves, kI8StageLoads>(1, w);
+      else
+        wait_vmcnt<0>();
+    };
+    issue(0);
+    if (1 < ntiles) issue(1);
+    wait_codes(0);
+    lds_write_barrier();  // tile 0's codes landed
+    if (!SCORE) convert(0);
+    lds_write_barrier();  // tile 0 converted, its code stage free
+    if (2 < ntiles) issue(2);
+    // step 0: scores only (and tile 1's conversion)
+    if (1 < ntiles) wait_codes(1);
+    lds_write_barrier();  // B1(0)
+    if (SCORE)
+      score_tile(0, lim_of(x0, 0), lim_of(x1, 0));
+    else if (1 < ntiles)
+      convert(1);
+    lds_write_barrier();  // B2(0)
+    if (3 < ntiles) issue(3);
+    if (SCORE) {
+      mx_mine[0] = mx0;
+      mx_mine[64] = mx1;
+    }
+    for (int k = 1; k < ntiles; ++k) {
+      if (k + 1 < ntiles) wait_codes(k + 1);
+      lds_write_barrier();  // B1(k)
+      if (SCORE) {
+        score_step(std::true_type{}, k, k - 1, lim_of(x0, k), lim_of(x1, k));
+      } else {
+        // the conversion first: the V fragments' 64 registers are not live across it
+        if (k + 1 < ntiles) convert(k + 1);
+        values_fetch(cvt_of(k - 1), lane, hh, vb);
+      }
+      lds_write_barrier();  // B2(k): probabilities published, tile k + 1's code stage free
+      if (k + 3 < ntiles) issue(k + 3);
+      if (SCORE) {
+        mx_mine[0] = mx0;
+        mx_mine[64] = mx1;
+      } else {
+        value_step();
+      }
+    }
+    lds_write_barrier();  // B1'
+    if (SCORE)
+      score_step(std::false_type{}, -1, ntiles - 1, 0, 0);
+    else
+      values_fetch(cvt_of(ntiles - 1), lane, hh, vb);
+    if (SCORE)
+      lds_write_barrier();  // B2'
+    else
+      lds_barrier();
+    if (!SCORE) value_step();
+  }
+
+  lds_write_barrier();
+  float s0 = 0.f, s1 = 0.f;
+  if (SCORE) {
+    wait_vmcnt<0>();
+    s0 = wave_sum_rows(l0);
+    s1 = wave_sum_rows(l1);
+    mx_mine[0] = s0;
+    mx_mine[64] = s1;
+  }
+  lds_write_barrier();
+  if (SCORE) {
+    const float t0 = s0 + mx_part[0], t1 = s1 + mx_part[64];
+    if (hh == 0) {
+      al_row[0] = t0 > 0.f ? 1.0f / t0 : 0.f;
+      al_row[64] = t1 > 0.f ? 1.0f / t1 : 0.f;
+      if (g == 0) {
+        if (x0.ok) a.lse[x0.qrow] = t0 > 0.f ? (m0 + fast_log2(t0)) * kLn2 : -INFINITY;
+        if (x1.ok) a.lse[x1.qrow] = t1 > 0.f ? (m1 + fast_log2(t1)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+  lds_write_barrier();
+  if (!SCORE) {
+    const float inv0 = al_row[0], inv1 = al_row[64];
+    const int col = (kDv / 2) * hh + 4 * g;
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+      const QRow& x = jq == 0 ? x0 : x1;
+      if (x.ok) {
+        uint16_t* dst = a.out + (size_t)x.qrow * kDv + col;
+#pragma unroll
+        for (int ct = 0; ct < kOHalf; ++ct) {
+          const f32x4 v = (jq == 0 ? o0[ct] : o1[ct]) * (jq == 0 ? inv0 : inv1);
+          bf16x4 h;
+          h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+          *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
+        }
+      }
+    }
+  }
+}
+
+template <int CODE>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws_codes(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[3 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t codes_raw[2 * kI8StageBytes];
+  __shared__ __attribute__((aligned(16))) float tsc_raw[3 * kTileRows];
+  __shared__ __attribute__((aligned(16))) float mx_raw[4 * 2 * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t pb_raw[2 * 2 * 64 * 16];
+  __shared__ __attribute__((aligned(16))) float al_raw[2 * 2 * 64];
+  __shared__ int s_pid[kPWin];
+  __shared__ int s_tile;
+  const WsCodesLds L{(MLA_LDS uint8_t*)codes_raw, (MLA_LDS uint8_t*)cvt_raw, (MLA_LDS float*)tsc_raw,
+                     (MLA_LDS float*)mx_raw,      (MLA_LDS uint8_t*)pb_raw,  (MLA_LDS float*)al_raw, s_pid};
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int total_tiles = a.tile_cum[a.batch];
+  const int block_rows = a.tok_per_tile * a.heads;
+  const int row_blocks = (block_rows + kBlockRows - 1) / kBlockRows;
+  for (;;) {
+    __syncthreads();
+    if (threadIdx.x == 0) s_tile = atomicAdd(a.counter, 1);
+    __syncthreads();
+    const int t = s_tile;
+    if (t >= total_tiles) break;
+    const WorkTile wt = locate_work(a, t, row_blocks);
+    if (w < 4)
+      ws_codes_work_tile<true, CODE>(a, wt, L, w, lane, block_rows);
+    else
+      ws_codes_work_tile<false, CODE>(a, wt, L, w, lane, block_rows);
+  }
+}
+
 hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream) {
   hipLaunchKernelGGL(prefill_worklist, dim3(1), dim3(256), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (kv_dtype == 1)
-    hipLaunchKernelGGL(prefill_persistent_codes<kCodeInt8>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL(prefill_persistent_ws_codes<kCodeInt8>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   else if (kv_dtype == 2)
-    hipLaunchKernelGGL(prefill_persistent_codes<kCodeFp8>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL(prefill_persistent_ws_codes<kCodeFp8>, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   else
     hipLaunchKernelGGL(prefill_persistent_ws, dim3(plan.grid), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();
