@@ -27,7 +27,7 @@
 
 namespace mla {
 
-constexpr int kPWin = 128;  // page ids staged per window
+constexpr int kPWin = 256;  // page ids staged per window (a pipeline restart per window)
 
 __device__ __forceinline__ int p_clamp(int L, int max_pages) {
   L = L < 0 ? 0 : L;
