@@ -281,14 +281,15 @@ __device__ __forceinline__ void convert_code_tile(const MLA_LDS uint8_t* stage, 
   static_assert(kUnits > (kPer - 1) * kThreads, "only the last round of units is partial");
   typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
   u32x2_t x[kPer];
+  constexpr bool kEven = kUnits % kThreads == 0;  // then no lane needs a bounds test
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (i < kPer - 1 || tid + i * kThreads < kUnits)
+    if (kEven || i < kPer - 1 || tid + i * kThreads < kUnits)
       x[i] = *reinterpret_cast<const MLA_LDS u32x2_t*>(stage + 8 * (tid + i * kThreads));
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int u = tid + i * kThreads;
-    if (i < kPer - 1 || u < kUnits) {
+    if (kEven || i < kPer - 1 || u < kUnits) {
       const int t = u / kRowUnits, j = u - kRowUnits * t;
       u32x4 o;
       o[0] = codepair_to_bf16<CODE, 0>(x[i][0]); o[1] = codepair_to_bf16<CODE, 1>(x[i][0]);
