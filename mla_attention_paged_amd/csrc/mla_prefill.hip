@@ -242,6 +242,9 @@ __device__ __forceinline__ void values_mfma(const bf16x4 (&vb)[kOHalf][2], bf16x
 // before the softmax, which covers their latency.
 constexpr int kKAhead = 6;
 
+// Waves that issue the bf16 tile loads (the value waves, the last four).
+constexpr int kLoadWaves = 4;
+
 // A query row of a work tile: row r of the tile is head r % heads of token
 // j0 + r / heads.
 struct QRow {
@@ -359,21 +362,32 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
     __builtin_amdgcn_s_waitcnt(0);  // the page ids are in LDS (and every earlier load has landed)
     lds_barrier();
     const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
-    auto issue = [&](int k) {
+    // Only the value waves issue tile loads (kLoadWaves of them), so the
+    // score waves start each step on their K reads; the page id of the next
+    // tile to issue is read from LDS one step ahead.
+    int pid_next = 0;
+    auto issue = [&](int k, int pid) {
       const int p = k >> 1;
-      stage_tile<kWaves>(a.kv + (size_t)L.pid[p] * kPageBytes, k & 1, wt.kv_end - kPage * (plo + p), stage(k), w,
-                         lane);
+      stage_tile<kLoadWaves>(a.kv + (size_t)pid * kPageBytes, k & 1, wt.kv_end - kPage * (plo + p), stage(k),
+                             w - (kWaves - kLoadWaves), lane);
     };
     auto lim_of = [&](const QRow& x, int k) { return x.ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
     auto wait_for = [&](int k) {  // tile k landed; tile k + 1 may stay in flight
-      if (k + 1 < ntiles) wait_tile<kWaves>(1, w); else wait_vmcnt<0>();
+      if (SCORE) return;
+      if (k + 1 < ntiles) wait_tile<kLoadWaves>(1, w - (kWaves - kLoadWaves)); else wait_vmcnt<0>();
     };
-    issue(0);
-    if (1 < ntiles) issue(1);
+    if (!SCORE) {
+      issue(0, L.pid[0]);
+      if (1 < ntiles) issue(1, L.pid[0]);
+      pid_next = L.pid[1 < n ? 1 : 0];
+    }
     // step 0: scores only
     wait_for(0);
     lds_write_barrier();  // B1(0)
-    if (2 < ntiles) issue(2);
+    if (!SCORE && 2 < ntiles) {
+      issue(2, pid_next);
+      pid_next = L.pid[min(3, 2 * n - 1) >> 1];
+    }
     if (SCORE) {
       f32x4 c0, c1;
       scores_2q(stage(0), q0, q1, lane, hh, c0, c1);
@@ -388,7 +402,10 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
     for (int k = 1; k < ntiles; ++k) {
       wait_for(k);
       lds_write_barrier();  // B1(k)
-      if (k + 2 < ntiles) issue(k + 2);
+      if (!SCORE && k + 2 < ntiles) {
+        issue(k + 2, pid_next);
+        pid_next = L.pid[min(k + 3, 2 * n - 1) >> 1];
+      }
       if (SCORE)
         score_step(std::true_type{}, k, lim_of(x0, k), lim_of(x1, k));
       else
