@@ -225,8 +225,15 @@ __device__ __forceinline__ void values_fetch(const MLA_LDS uint8_t* tile, int la
   }
 }
 
-__device__ __forceinline__ void values_mfma(const bf16x4 (&vb)[kOHalf][2], bf16x8 p0, bf16x8 p1,
-                                            f32x4 (&o0)[kOHalf], f32x4 (&o1)[kOHalf]) {
+// With `next` (the following tile's stage), each column tile's two V
+// fragments are re-read from it as soon as its MFMAs have taken them, so
+// the next tile's V reads overlap this tile's value MFMAs.
+template <bool REFILL>
+__device__ __forceinline__ void values_mfma(bf16x4 (&vb)[kOHalf][2], bf16x8 p0, bf16x8 p1, f32x4 (&o0)[kOHalf],
+                                            f32x4 (&o1)[kOHalf], const MLA_LDS uint8_t* next, int lane, int ch) {
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+  const MLA_LDS uint8_t* vbase = next + (4 * g + (i16 >> 2)) * kLdsPitch + 4 * (i16 & 3) * 2 + 512 * ch;
 #pragma unroll
   for (int ct = 0; ct < kOHalf; ++ct) {
     const bf16x4 v0 = vb[ct][0], v1 = vb[ct][1];
@@ -235,6 +242,10 @@ __device__ __forceinline__ void values_mfma(const bf16x4 (&vb)[kOHalf][2], bf16x
     va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
     o0[ct] = mfma16x16x32(va, p0, o0[ct]);
     o1[ct] = mfma16x16x32(va, p1, o1[ct]);
+    if constexpr (REFILL) {
+      vb[ct][0] = lds_tr16(vbase + 32 * ct);
+      vb[ct][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * ct);
+    }
   }
 }
 
@@ -339,8 +350,9 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
       mx1 = mask_half(b0 + b1, hh, lim1, a.scale_log2, lane, sp1);
     }
   };
-  // value waves: the value product of the fetched tile from the published probabilities
-  auto value_step = [&]() {
+  // value waves: the value product of the tile in vb from the published
+  // probabilities; with REFILL, vb is re-read from the stage of tile `next`
+  auto value_step = [&](auto refill, int next) {
     const bf16x8 p0 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row);
     const bf16x8 p1 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row + 64 * 16);
     const float al0 = al_row[0], al1 = al_row[64];
@@ -351,7 +363,7 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
         o1[ct] *= al1;
       }
     }
-    values_mfma(vb, p0, p1, o0, o1);
+    values_mfma<decltype(refill)::value>(vb, p0, p1, o0, o1, stage(next), lane, hh);
   };
 
   for (int plo = 0; plo < wt.npages; plo += kPWin) {
@@ -398,6 +410,8 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
     if (SCORE) {
       mx_mine[0] = mx0;
       mx_mine[64] = mx1;
+    } else {
+      values_fetch(stage(0), lane, hh, vb);  // V of tile 0
     }
     for (int k = 1; k < ntiles; ++k) {
       wait_for(k);
@@ -406,12 +420,9 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
         issue(k + 2, pid_next);
         pid_next = L.pid[min(k + 3, 2 * n - 1) >> 1];
       }
-      if (SCORE)
-        score_step(std::true_type{}, k, lim_of(x0, k), lim_of(x1, k));
-      else
-        values_fetch(stage(k - 1), lane, hh, vb);
+      if (SCORE) score_step(std::true_type{}, k, lim_of(x0, k), lim_of(x1, k));
       // B2(k): the probabilities and factors are written; the value waves'
-      // V reads may stay in flight
+      // V reads of tile k may stay in flight
       if (SCORE)
         lds_write_barrier();
       else
@@ -420,20 +431,17 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
         mx_mine[0] = mx0;
         mx_mine[64] = mx1;
       } else {
-        value_step();
+        value_step(std::true_type{}, k);  // tile k - 1, then V of tile k into vb
       }
     }
     // the window's last tile
     lds_write_barrier();  // B1'
-    if (SCORE)
-      score_step(std::false_type{}, -1, 0, 0);
-    else
-      values_fetch(stage(ntiles - 1), lane, hh, vb);
+    if (SCORE) score_step(std::false_type{}, -1, 0, 0);
     if (SCORE)  // B2'
       lds_write_barrier();
     else
       lds_barrier();
-    if (!SCORE) value_step();
+    if (!SCORE) value_step(std::false_type{}, 0);
   }
 
   // row totals: each score wave holds the sums of its own tile rows
@@ -655,7 +663,7 @@ __device__ __forceinline__ void ws_codes_work_tile(const PrefillArgs& a, const W
         o1[ct] *= al1;
       }
     }
-    values_mfma(vb, p0, p1, o0, o1);
+    values_mfma<false>(vb, p0, p1, o0, o1, nullptr, lane, hh);
   };
   // value waves: convert tile kk's codes (256 threads)
   auto convert = [&](int kk) {
