@@ -135,14 +135,18 @@ constexpr int kPFStages = 4;
 //    rescale factors, and compute the scores of tile k (the first six K
 //    fragments are requested before the softmax, which covers their
 //    latency); after B2(k) they publish tile k's row max;
-//  - value waves: before B2(k), while the score waves work, request all 32
-//    transposed V fragments of tile k-1 (64 registers); after B2(k),
-//    rescale and run the value product's 32 MFMAs back to back.
-// Each phase has one active wave per SIMD, so each wave hides its own LDS
-// latency: measured, the fetch-ahead made the kernel 9% faster.
+//  - value waves: at B1(k) issue every load of tile k + 2 (the score waves
+//    issue none, so they start on their K reads at once); after B2(k),
+//    rescale and run the value product of tile k - 1 from the 32
+//    transposed V fragments in registers, re-reading each fragment from
+//    tile k's stage as soon as its two MFMAs have taken it.
+// The V reads of tile k thus overlap the value MFMAs of tile k - 1 and stay
+// out of the score phase: measured, V reads that run into the score waves'
+// K reads slow the whole step, so B1 waits for them.
 // Each score wave keeps the row sums of its own 16 rows of every tile; the
-// two halves are added at the end of the work tile.  Stages k (scores) and
-// k-1 (values) are read during step k while k+1 and k+2 load.
+// two halves are added at the end of the work tile.  Stages k (scores and V
+// reads) and k - 1 (V in registers) are in use during step k while k + 1
+// and k + 2 load.
 // ---------------------------------------------------------------------------
 
 // Scores of this wave's 16 tile rows against two 16-row query tiles: each K
