@@ -103,14 +103,19 @@ def test_decode_plan_shapes(lib):
     # 64K-row decode, 4 requests: one phase-one workgroup per compute unit
     g, ws = mla.mla_decode_plan(4, 16, 4, 65536, 0, num_cus=256)
     assert g == 256 and ws >= (256 + 4) * 64 * (512 * 2 + 4)  # bf16 partial outputs + fp32 log2-sum-exp
-    # 256 rows: a single workgroup writes the output directly, no workspace
-    assert mla.mla_decode_plan(1, 16, 1, 256, 0, num_cus=256) == (1, 0)
-    # at least four pages per workgroup
+    # 256 rows (four pages): one workgroup per page, partials and a merge
+    g, ws = mla.mla_decode_plan(1, 16, 1, 256, 0, num_cus=256)
+    assert g == 4 and ws >= (4 + 1) * 16 * (512 * 2 + 4)
+    # one page: a single workgroup writes the output directly, no workspace
+    assert mla.mla_decode_plan(1, 16, 1, 64, 0, num_cus=256) == (1, 0)
+    # at least one page per workgroup, at most one workgroup per compute unit
     g, _ = mla.mla_decode_plan(2, 16, 1, 640, 0, num_cus=256)
-    assert g == 5
+    assert g == 20
+    g, _ = mla.mla_decode_plan(2, 16, 1, 640, 0, num_cus=8)
+    assert g == 8
     # more rows per request (q_len * heads > 64) still plans
     g, ws = mla.mla_decode_plan(2, 32, 4, 8192, 0, num_cus=256)
-    assert g == 64 and ws > 0
+    assert g == 256 and ws > 0
 
 
 def test_workspace_size_is_monotone_and_covers_plan(lib):
