@@ -48,8 +48,11 @@ __global__ __launch_bounds__(256, 2) void nt_gemm(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int i16 = lane & 15, gq = lane >> 4;
-  const size_t h = blockIdx.y;
-  const int m0 = blockIdx.x * kGemmRows;
+  // x: head, y: token block, so that the workgroups running together cover
+  // the heads of neighbouring tokens (contiguous memory in [token, head, k]
+  // rows) rather than one head's rows a head-stride apart
+  const size_t h = blockIdx.x;
+  const int m0 = blockIdx.y * kGemmRows;
   const uint16_t* A = g.a + h * g.a_head;
   const uint16_t* B = g.bt + h * g.b_head;
 
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void nt_gemm(GemmArgs g) {
 
 hipError_t launch_gemm(const GemmArgs& g, int heads, hipStream_t stream) {
   if (g.m <= 0) return hipSuccess;
-  const dim3 grid((g.m + kGemmRows - 1) / kGemmRows, heads);
+  const dim3 grid(heads, (g.m + kGemmRows - 1) / kGemmRows);
   if (g.n == 512 && g.k == 128)
     hipLaunchKernelGGL((nt_gemm<512, 128, 2, false>), grid, dim3(256), 0, stream, g);
   else if (g.n == 128 && g.k == 512)
