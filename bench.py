@@ -34,8 +34,8 @@ baseline, not a target.  The prefill leg carries its own: the oracle on
 Besides the headline means (events around the whole timed region), the
 decode and prefill legs report per-call p10 / p50 / p90 from events around
 each call (100 and 20 calls; the events add about 2 us per call), and the
-JSON records rocm-smi's sclk / mclk before the GPU is touched and after the
-run.
+JSON records the cards' current sclk / mclk levels (amdgpu sysfs) before the GPU
+is touched and after the run.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
                        [--no-cpu-baseline] [--prefill-steps P] [--calib-copy-mb M]
@@ -120,18 +120,27 @@ def time_each(fn_list, stream, n: int) -> dict:
 
 
 def gpu_clocks():
-    """sclk / mclk of the cards as rocm-smi reports them (None when it is not available)."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30,
-                           close_fds=True)
-        d = json.loads(r.stdout)
-    except Exception:
-        return None
+    """Current sclk / mclk level of each card from the amdgpu sysfs tables (pp_dpm_sclk,
+    pp_dpm_mclk: the level marked '*'), or None when they are not readable.  Read from
+    files, so that no child program is started from this (possibly profiled) process."""
+    import glob
+    import re
     out = {}
-    for card, v in d.items():
-        if isinstance(v, dict):
-            out[card] = {k: x for k, x in v.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        card = os.path.basename(os.path.dirname(dev))
+        if not re.fullmatch(r"card\d+", card):
+            continue
+        rec = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*") and ":" in line:
+                            rec[name[len("pp_dpm_"):]] = line.split(":", 1)[1].replace("*", "").strip()
+            except OSError:
+                pass
+        if rec:
+            out[card] = rec
     return out or None
 
 
