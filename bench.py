@@ -308,8 +308,8 @@ def main() -> int:
         return record_traffic(args.record_traffic[0], args.record_traffic[1], args.calib_copy_mb or 1024)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how the decode would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library runs each call on a single GPU and has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         return 2
 
     clocks_before = gpu_clocks()  # before this process touches the GPU
