@@ -303,6 +303,17 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
   MLA_LDS uint8_t* const pb_row = L.pb + (128 * rg + lane) * 16;  // query tile j: + 64 * 16 * j
   MLA_LDS float* const al_row = L.al + 128 * rg + lane;           // query tile j: + 64 * j
 
+  // value waves: the byte offsets (within a half page, row t of the half)
+  // of this lane's slot in each of the wave's tile loads (load i = lw + 4 j)
+  // are the same for every tile; full tiles use them as they are
+  constexpr int kMyLoads = (kStageLoads + kLoadWaves - 1) / kLoadWaves;  // 10
+  const int lw = __builtin_amdgcn_readfirstlane(w - (kWaves - kLoadWaves));  // wave-uniform
+  int ld_off[kMyLoads];
+  if (!SCORE) {
+#pragma unroll
+    for (int j = 0; j < kMyLoads; ++j) ld_off[j] = stage_src(lw + kLoadWaves * j, lane, 0, kTileRows);
+  }
+
   // score-wave state
   bf16x8 q0[kQFrags], q1[kQFrags];
   float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f, mx0 = -INFINITY, mx1 = -INFINITY;
@@ -384,8 +395,19 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
     int pid_next = 0;
     auto issue = [&](int k, int pid) {
       const int p = k >> 1;
-      stage_tile<kLoadWaves>(a.kv + (size_t)pid * kPageBytes, k & 1, wt.kv_end - kPage * (plo + p), stage(k),
-                             w - (kWaves - kLoadWaves), lane);
+      const int half = k & 1;
+      const int rem = wt.kv_end - kPage * (plo + p);
+      const uint8_t* page = a.kv + (size_t)pid * kPageBytes;
+      if (rem >= kTileRows * (half + 1)) {  // every row of the tile is the request's
+        const uint8_t* hbase = page + (size_t)half * kTileRows * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < kMyLoads; ++j) {
+          const int i = lw + kLoadWaves * j;
+          if (i < kStageLoads) lds_dma16(hbase, ld_off[j], stage(k) + i * 1024);
+        }
+      } else {
+        stage_tile<kLoadWaves>(page, half, rem, stage(k), lw, lane);
+      }
     };
     auto lim_of = [&](const QRow& x, int k) { return x.ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
     auto wait_for = [&](int k) {  // tile k landed; tile k + 1 may stay in flight
