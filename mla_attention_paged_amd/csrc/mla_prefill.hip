@@ -132,8 +132,8 @@ constexpr int kPFStages = 4;
 //    B2(k-1)), finish the softmax of tile k-1 for their own 16 rows of it
 //    (the two partners use the same max, so they make the same rescale
 //    decisions), write their half of the probability fragments and the
-//    rescale factors, and compute the scores of tile k (the first six K
-//    fragments are requested before the softmax, which covers their
+//    rescale factors, and compute the scores of tile k (the first kKAhead
+//    K fragments are requested before the softmax, which covers their
 //    latency); after B2(k) they publish tile k's row max;
 //  - value waves: at B1(k) issue every load of tile k + 2 (the score waves
 //    issue none, so they start on their K reads at once); after B2(k),
