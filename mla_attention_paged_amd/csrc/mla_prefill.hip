@@ -592,7 +592,7 @@ __device__ __forceinline__ bf16x4 softmax_half_sc(const f32x4& s, f32x4 sc, floa
   return p;
 }
 
-constexpr int kKAheadC = 4;
+constexpr int kKAheadC = 3;
 
 struct WsCodesLds {
   MLA_LDS uint8_t* codes;  // two code stages
