@@ -25,26 +25,37 @@ The absorption leg times ``mla_q_absorb`` and ``mla_v_up`` on 8,629 tokens x
 byte), so GB/s of algorithmic bytes (inputs and weights read once, outputs
 written once) against HBM is the one that bounds them.
 
+The other decode workloads (``configs``: the 256-row latency case, the
+ragged 16-request batch with 32 heads, the 256K-row INT8 batch) are timed
+the same way, each after a fixed warm-up of its own (0.25 s of its calls,
+whatever --warmup says), with two or three cache copies rotated (the
+256-row case is deliberately cache-hot).
+
 The CPU baseline is the fp64 oracle on the host's cores (at most 16
 threads), timed on the full decode workload (all 16 query tokens, all
 heads), repeated until about 10 s of CPU work have run; it is a reported
-baseline, not a target.  The prefill leg carries its own: the oracle on
-128 seeded new tokens (all heads), in TFLOP/s of those tokens' flops.
+baseline, not a target.  Each other decode workload carries its own (the
+whole call, once); the prefill leg carries the oracle on 128 seeded new
+tokens (all heads), in TFLOP/s of those tokens' flops.
 
 Besides the headline means (events around the whole timed region), the
-decode and prefill legs report per-call p10 / p50 / p90 from events around
-each call (100 and 20 calls; the events add about 2 us per call), and the
-JSON records the cards' current sclk / mclk levels (amdgpu sysfs) before the GPU
-is touched and after the run.
+decode and prefill legs report the spread of block means: the timed region
+split into blocks of back-to-back calls with events only at block edges
+(events between single calls add a launch gap to every call).  Before its
+W warm-up steps the headline leg runs a fixed 0.25 s of the same calls, so
+that the shader clock has ramped up after the idle input generation.  The
+JSON records the cards' current sclk / mclk levels (amdgpu sysfs) before
+the GPU is touched and after the run.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill]
                        [--no-cpu-baseline] [--prefill-steps P] [--calib-copy-mb M]
        python bench.py --record-traffic FETCH_DIR WRITE_DIR [--calib-copy-mb M]
 
-The roofline's ``traffic`` is the HBM bytes per decode call read from
-profiles/mla_decode_b4_h16_q4_L64K_traffic.json (written by --record-traffic from two
-rocprofv3 counter runs); it is null when the kernel sources have changed
-since those counters were taken.
+The rooflines' ``traffic`` is the HBM bytes per call read from
+profiles/mla_decode_b4_h16_q4_L64K_traffic.json and
+profiles/mla_prefill_b8_h16_P16K-96K_N200-2000_traffic.json (written by --record-traffic
+from two rocprofv3 counter runs); it is null when the kernel sources have changed since
+those counters were taken.
 """
 from __future__ import annotations
 
@@ -102,21 +113,43 @@ def prefill_algorithmic_bytes(case) -> int:
     return int(L.sum() * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4)
 
 
-def time_each(fn_list, stream, n: int) -> dict:
-    """Per-call spread: HIP events on `stream` between consecutive calls (fn_list[i % len]),
-    n calls; p10 / p50 / p90 microseconds.  The events add a little to each call; the
-    headline figures come from time_calls (no events between calls)."""
+def block_spread(fn_list, stream, blocks: int, per_block: int) -> dict:
+    """Spread of the per-call time: `blocks` blocks of `per_block` back-to-back calls
+    (fn_list[i % len]), HIP events on `stream` only at block edges; min / median / max of
+    the blocks' mean microseconds per call."""
     import torch
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    k = 0
     with torch.cuda.stream(stream):
-        for i in range(n):
-            ev[i].record(stream)
-            fn_list[i % len(fn_list)]()
-        ev[n].record(stream)
+        ev[0].record(stream)
+        for b in range(blocks):
+            for _ in range(per_block):
+                fn_list[k % len(fn_list)]()
+                k += 1
+            ev[b + 1].record(stream)
     torch.cuda.synchronize()
-    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
-    p10, p50, p90 = np.percentile(us, [10, 50, 90])
-    return {"p10": round(float(p10), 2), "p50": round(float(p50), 2), "p90": round(float(p90), 2), "n": n}
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / per_block for i in range(blocks)])
+    return {"min": round(float(us.min()), 2), "median": round(float(np.median(us)), 2),
+            "max": round(float(us.max()), 2), "blocks": blocks, "calls_per_block": per_block}
+
+
+def warm(fn_list, stream, seconds: float) -> int:
+    """Run fn_list[i % len] back to back on `stream` for about `seconds` of wall time (the
+    shader clock ramps up over the first tenths of a second of work after an idle stretch);
+    returns the number of calls."""
+    import torch
+    t0 = time.time()
+    n = 0
+    batch = 4
+    while True:
+        with torch.cuda.stream(stream):
+            for _ in range(batch):
+                fn_list[n % len(fn_list)]()
+                n += 1
+        torch.cuda.synchronize()
+        if time.time() - t0 >= seconds:
+            return n
+        batch = min(2 * batch, 256)
 
 
 def gpu_clocks():
@@ -164,13 +197,22 @@ def time_calls(fn_list, stream, warmup: int, steps: int) -> float:
     return t0.elapsed_time(t1)
 
 
-# the sources that shape the decode call's kernels and plan (its recorded HBM traffic is
-# dropped when the code of any of them changes; comments do not count)
-KERNEL_SOURCES = ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_decode.hip",
-                  "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h"]
-COUNTER_RUN_FLAGS = ("--steps 5 --warmup 20 --no-prefill --no-append --no-cpu-baseline --no-absorb --no-pages "
-                     "--no-varlen --no-scaled")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_decode_b4_h16_q4_L64K_traffic.json")
+# The sources that shape each leg's kernels and plan (its recorded HBM traffic is dropped
+# when the code of any of them changes; comments do not count).
+KERNEL_SOURCES = {
+    "decode": ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_decode.hip",
+               "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h"],
+    "prefill": ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_prefill.hip",
+                "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h"],
+}
+# kernels whose counter readings make up one call of each leg
+LEG_KERNELS = {"decode": ("mla::decode_phase1_pipe", "mla::decode_merge"),
+               "prefill": ("mla::prefill_worklist", "mla::prefill_persistent_ws(")}
+COUNTER_RUN_FLAGS = ("--steps 5 --warmup 20 --prefill-steps 2 --no-configs --no-append --no-cpu-baseline "
+                     "--no-absorb --no-pages --no-varlen --no-scaled --no-scaled-prefill")
+TRAFFIC_FILES = {"decode": os.path.join(ROOT, "profiles", "mla_decode_b4_h16_q4_L64K_traffic.json"),
+                 "prefill": os.path.join(ROOT, "profiles", "mla_prefill_b8_h16_P16K-96K_N200-2000_traffic.json")}
+LEG_WORKLOAD = {"decode": 1, "prefill": 3}
 
 
 def strip_comments(src: str) -> str:
@@ -198,26 +240,25 @@ def strip_comments(src: str) -> str:
     return "\n".join(ln for ln in lines if ln)
 
 
-def sources_digest() -> str:
-    """SHA-256 of the code (comments stripped) of the sources that shape the decode call."""
+def sources_digest(leg: str = "decode") -> str:
+    """SHA-256 of the code (comments stripped) of the sources that shape a leg's call."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[leg]:
         with open(os.path.join(ROOT, rel)) as f:
             h.update(strip_comments(f.read()).encode())
     return h.hexdigest()
 
 
-
-def recorded_traffic(workload: str):
-    """HBM bytes per decode call from the committed counter runs (FETCH_SIZE + WRITE_SIZE,
+def recorded_traffic(leg: str, workload: str):
+    """HBM bytes per call of a leg from the committed counter runs (FETCH_SIZE + WRITE_SIZE,
     calibrated against a plain copy), or None when the kernels changed since they were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[leg]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != sources_digest() or rec.get("workload") != workload:
+    if rec.get("source_sha256") != sources_digest(leg) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_call")
 
@@ -242,40 +283,122 @@ def _counter_means(path: str):
 
 
 def record_traffic(fetch_dir: str, write_dir: str, calib_mb: int) -> int:
-    """Turn the FETCH_SIZE and WRITE_SIZE runs of this script (with --calib-copy-mb) into
-    profiles/mla_decode_b4_h16_q4_L64K_traffic.json: HBM bytes per decode call, each counter scaled by the
-    factor that maps its reading of the calibration copy onto the copy's true size."""
+    """Turn the FETCH_SIZE and WRITE_SIZE runs of this script (with --calib-copy-mb) into the
+    traffic records of the decode and prefill legs: HBM bytes per call, each counter scaled by
+    the factor that maps its reading of the calibration copy onto the copy's true size."""
+    import synth
     calib = calib_mb * (1 << 20)
     fetch, fcopy = _counter_means(fetch_dir)
     write, wcopy = _counter_means(write_dir)
     ffac = calib / (fcopy * 1024.0)
     wfac = calib / (wcopy * 1024.0)
-    per_kernel = {}
-    total = 0.0
-    for name in sorted(set(fetch) | set(write)):
-        if not (name.startswith("mla::decode_phase1_pipe") or name.startswith("mla::decode_merge")):
+    for leg, prefixes in LEG_KERNELS.items():
+        per_kernel = {}
+        total = 0.0
+        for name in sorted(set(fetch) | set(write)):
+            if not any(name.startswith(p) for p in prefixes):
+                continue
+            fb = fetch.get(name, 0.0) * 1024.0 * ffac
+            wb = write.get(name, 0.0) * 1024.0 * wfac
+            per_kernel[name] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
+            total += fb + wb
+        if not per_kernel:
             continue
-        fb = fetch.get(name, 0.0) * 1024.0 * ffac
-        wb = write.get(name, 0.0) * 1024.0 * wfac
-        per_kernel[name] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
-        total += fb + wb
-    import synth
-    rec = {"workload": synth.make_workload(1).name, "source_sha256": sources_digest(),
-           "source_digest": "SHA-256 of the decode sources' code, comments stripped (bench.strip_comments)",
-           "hbm_bytes_per_call": round(total), "per_kernel": per_kernel,
-           "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
-           "calibration": f"plain device copy of {calib_mb} MiB (torch copy_), largest copy dispatch reading",
-           "commands": [f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -f csv -d {fetch_dir} -o fetch -- "
-                        f"python3 bench.py {COUNTER_RUN_FLAGS} --calib-copy-mb {calib_mb}",
-                        f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -f csv -d {write_dir} -o write -- "
-                        f"python3 bench.py {COUNTER_RUN_FLAGS} --calib-copy-mb {calib_mb}",
-                        f"python3 bench.py --record-traffic {fetch_dir} {write_dir} --calib-copy-mb {calib_mb}"]}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
-        f.write("\n")
-    print(json.dumps(rec))
+        rec = {"workload": synth.WORKLOADS[LEG_WORKLOAD[leg]]["name"], "source_sha256": sources_digest(leg),
+               "source_digest": f"SHA-256 of the {leg} sources' code, comments stripped (bench.strip_comments)",
+               "hbm_bytes_per_call": round(total), "per_kernel": per_kernel,
+               "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
+               "calibration": f"plain device copy of {calib_mb} MiB (torch copy_), largest copy dispatch reading",
+               "commands": [f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -f csv -d {fetch_dir} -o fetch -- "
+                            f"python3 bench.py {COUNTER_RUN_FLAGS} --calib-copy-mb {calib_mb}",
+                            f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -f csv -d {write_dir} -o write -- "
+                            f"python3 bench.py {COUNTER_RUN_FLAGS} --calib-copy-mb {calib_mb}",
+                            f"python3 bench.py --record-traffic {fetch_dir} {write_dir} --calib-copy-mb {calib_mb}"]}
+        os.makedirs(os.path.dirname(TRAFFIC_FILES[leg]), exist_ok=True)
+        with open(TRAFFIC_FILES[leg], "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
     return 0
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    """Threads the oracle baseline runs with: the CPUs this process may use, at most 16
+    (a one-GPU machine's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def decode_leg(mla, torch, stream, case, copies: int, steps: int, warm_s: float, hot: bool = False) -> dict:
+    """Time mla_decode on `case` (resident inputs; `copies` cache copies rotated unless hot),
+    after `warm_s` seconds of warm-up calls; algorithmic GB/s, TFLOP/s and roofline fractions."""
+    from mla_gpu import decode_inputs
+    d = decode_inputs(case)
+    kvs = [d["kv"]] + ([] if hot else [d["kv"].clone() for _ in range(max(0, copies - 1))])
+    T, H = case.total_q(), case.heads
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    wsb = mla.mla_splitkv_workspace_size(case.batch, H, case.q_len, T, case.max_seq_len, d["kind"])
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    grid, _ = mla.mla_decode_plan(case.batch, H, case.q_len, case.max_seq_len, d["kind"])
+
+    def make(kv):
+        def call():
+            mla.mla_decode(d["q"], kv, d["scale"], d["kind"], d["pt"], case.cache.max_pages, d["seq_lens"],
+                           case.batch, case.q_len, H, case.cache.page_size, case.max_seq_len, case.softmax_scale,
+                           out, lse, ws, ws.numel(), stream)
+        return call
+
+    calls = [make(kv) for kv in kvs]
+    nwarm = warm(calls, stream, warm_s)
+    ms = time_calls(calls, stream, 0, steps) / steps
+    nbytes = decode_algorithmic_bytes(case)
+    flops = decode_flops(case)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfl = flops / (ms * 1e-3) / 1e12
+    res = {"workload": case.name, "batch": case.batch, "heads": H, "q_len": case.q_len,
+           "kv_lens": "all " + str(int(case.seq_lens[0])) if len(set(case.seq_lens.tolist())) == 1
+           else f"{int(case.seq_lens.min())}-{int(case.seq_lens.max())} (sum {int(case.seq_lens.sum())})",
+           "kv_dtype": case.cache.kv_dtype, "us_per_call": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "tflops": round(tfl, 1),
+           "frac_mfma": round(tfl / BF16_PEAK_TFLOPS, 4), "algorithmic_bytes_per_call": nbytes,
+           "flops_per_call": flops, "phase1_workgroups": grid, "warmup_calls": nwarm, "steps": steps,
+           "kv_copies_rotated": 1 if hot else len(kvs), "spread_us": block_spread(calls, stream, 5, max(4, steps // 5))}
+    del kvs, d, ws, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def oracle_decode_baseline(case, nbytes: int, min_s: float = 0.0) -> dict:
+    """The fp64 oracle on the whole decode call (all query tokens, all heads), repeated until
+    `min_s` seconds of CPU work have run (at least once)."""
+    import oracle
+    nt = oracle_threads()
+    runs, cpu_s = 0, 0.0
+    while runs == 0 or (cpu_s < min_s and cpu_s / runs * (runs + 1) <= 3 * min_s):
+        t = time.time()
+        oracle.decode(case, nthreads=nt)
+        cpu_s += time.time() - t
+        runs += 1
+    return {"value": round(nbytes * runs / cpu_s / 1e9, 4), "unit": "GB/s", "cores": nt,
+            "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(), "kind": "oracle",
+            "seconds": round(cpu_s, 2), "runs": runs, "us_per_call": round(cpu_s / runs * 1e6, 1),
+            "sample": f"the full {case.name} call (all {case.total_q()} query tokens x {case.heads} heads), "
+                      f"fp64 C oracle, {runs} run(s), {nt} threads"}
 
 
 def main() -> int:
@@ -286,6 +409,8 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other decode workloads (256-row, ragged 16 x 32 heads, 256K-row INT8)")
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-absorb", action="store_true",
                     help="skip the query-absorption / value up-projection leg")
@@ -346,13 +471,14 @@ def main() -> int:
         return call
 
     calls = [make_call(kv) for kv in kv_copies]
+    ramp_calls = warm(calls, stream, 0.25)  # shader clock ramp after the idle input generation
     total_ms = time_calls(calls, stream, args.warmup, args.steps)
     ms_per_step = total_ms / args.steps
-    per_call = time_each(calls, stream, 100)
+    spread = block_spread(calls, stream, 10, 20)
     nbytes = decode_algorithmic_bytes(case)
     flops = decode_flops(case)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    traffic = recorded_traffic(case.name)
+    traffic = recorded_traffic("decode", case.name)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -368,7 +494,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": case.name, "batch": case.batch, "heads": H, "q_len": case.q_len,
                    "kv_len": int(case.seq_lens[0]), "page_size": 64, "kv_dtype": "bf16",
-                   "kv_copies_rotated": len(kv_copies), "phase1_workgroups": grid},
+                   "kv_copies_rotated": len(kv_copies), "phase1_workgroups": grid,
+                   "clock_ramp_calls_before_warmup": ramp_calls},
         # The decode call is the unit: its two kernels (phase one, about 88% of the time,
         # and the merge) run back to back on one stream and are timed together.
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -378,7 +505,7 @@ def main() -> int:
                      "algorithmic_bytes_per_call": nbytes,
                      "us_per_call": round(ms_per_step * 1e3, 2)},
         "decode_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
-        "per_call_us": per_call,
+        "spread_us": spread,
         "input_generation_s": round(gen_s, 1),
     }
 
@@ -403,21 +530,24 @@ def main() -> int:
         pflops = prefill_flops(pcase)
         pms = ptotal / args.prefill_steps
         tflops = pflops / (pms * 1e-3) / 1e12
-        p_per_call = time_each([pcall], stream, 20)
+        p_spread = block_spread([pcall], stream, 4, 2)
         result["prefill"] = {
             "workload": pcase.name, "total_new_tokens": PT, "heads": pcase.heads,
             "prefix_lens": pcase.prefix_lens.tolist(),
             "new_lens": np.diff(pcase.cu_seqlens_q).tolist(),
             "ms_per_call": round(pms, 3), "tflops": round(tflops, 2), "flops_per_call": pflops,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent)"},
-            "per_call_ms": {k: (round(v / 1e3, 3) if k != "n" else v) for k, v in p_per_call.items()},
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic("prefill", pcase.name),
+                         "algorithmic_bytes_per_call": prefill_algorithmic_bytes(pcase),
+                         "kernel": "mla_prefill_varlen call (prefill_worklist + prefill_persistent_ws)"},
+            "spread_ms": {k: (round(v / 1e3, 3) if k in ("min", "median", "max") else v)
+                          for k, v in p_spread.items()},
         }
         if not args.no_cpu_baseline:
             # the oracle on a seeded sample of the new tokens (all heads), per flop
             import oracle
-            cores = max(1, min(16, os.cpu_count() or 1))
+            cores = oracle_threads()
             sample = np.sort(np.random.default_rng(5).choice(PT, 128, replace=False)).astype(np.int32)
             cu = pcase.cu_seqlens_q
             req = np.searchsorted(cu, sample, side="right") - 1
@@ -427,10 +557,29 @@ def main() -> int:
             oracle.prefill(pcase, tokens=sample, nthreads=cores)
             cs = time.time() - t
             result["prefill"]["cpu_baseline"] = {
-                "value": round(sflops / cs / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "seconds": round(cs, 2),
+                "value": round(sflops / cs / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+                "host_cpus": os.cpu_count(), "kind": "oracle", "seconds": round(cs, 2),
+                "extrapolated_full_call_s": round(cs * pflops / sflops, 1),
                 "sample": f"128 seeded new tokens of {PT} (all {pcase.heads} heads), fp64 C oracle; "
                           f"{sflops} flops of the call's {pflops}"}
+
+    # ---------------- the other decode workloads ----------------
+    if not args.no_configs:
+        legs = {}
+        for k, steps, hot in ((0, 400, True), (2, 60, False), (4, 40, False)):
+            kcase = synth.make_workload(k)
+            legs[kcase.name] = decode_leg(mla, torch, stream, kcase, 2, steps, 0.25, hot=hot)
+            if k == 0:
+                legs[kcase.name]["note"] = "cache-resident latency case (one cache copy, not rotated)"
+            if not args.no_cpu_baseline:
+                legs[kcase.name]["cpu_baseline"] = oracle_decode_baseline(
+                    kcase, legs[kcase.name]["algorithmic_bytes_per_call"])
+            del kcase
+        result["configs"] = legs
+        # 128 folded rows (two row blocks per share): the same 64K cache as the headline shape
+        wcase = synth.make_decode_case(2, 4, 32, 4, seq_lens=[65536] * 4, name="decode_b4_h32_q4_L64K")
+        result["wide_rows_decode"] = decode_leg(mla, torch, stream, wcase, 3, 100, 0.25)
+        del wcase
 
     # ---------------- absorption and up-projection on the prefill workload's tokens ----------------
     if not args.no_absorb:
@@ -451,7 +600,8 @@ def main() -> int:
                 ("v_up", lambda: mla.mla_v_up(ao, wuv, vout, AT, AH, stream),
                  AT * AH * (512 + 128) * 2 + w_bytes)):
             n = 200
-            ms = time_calls([fn], stream, 2000, n) / n
+            warm([fn], stream, 0.25)
+            ms = time_calls([fn], stream, 0, n) / n
             fl = 2 * AT * AH * 128 * 512
             legs[name] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -477,8 +627,10 @@ def main() -> int:
                                    out, lse, ws, ws.numel(), stream)
                 return call
 
-            psteps = max(20, args.steps // 2)
-            pms = time_calls([make_pcall(kv) for kv in pkv], stream, args.warmup, psteps) / psteps
+            psteps = 100
+            pcalls = [make_pcall(kv) for kv in pkv]
+            warm(pcalls, stream, 0.25)
+            pms = time_calls(pcalls, stream, 0, psteps) / psteps
             pbytes = decode_algorithmic_bytes(pcase2)
             legs[str(ps)] = {"us_per_call": round(pms * 1e3, 2),
                              "GBps": round(pbytes / (pms * 1e-3) / 1e9, 1),
@@ -507,8 +659,10 @@ def main() -> int:
                                       vcase.softmax_scale, vout, vlse, vws, vws.numel(), stream)
             return call
 
-        vsteps = max(20, args.steps // 2)
-        vms = time_calls([make_vcall(kv) for kv in vkv], stream, args.warmup, vsteps) / vsteps
+        vsteps = 100
+        vcalls = [make_vcall(kv) for kv in vkv]
+        warm(vcalls, stream, 0.25)
+        vms = time_calls(vcalls, stream, 0, vsteps) / vsteps
         L = vcase.cache.kv_lens.astype(np.int64)
         vbytes = int(L.sum() * 1152 + vT * H * (576 * 2 + 512 * 2 + 4) + int(((L + 63) // 64).sum()) * 4
                      + vcase.batch * 8)
@@ -538,8 +692,10 @@ def main() -> int:
                                    scase.softmax_scale, out, lse, sws, sws.numel(), stream)
                 return call
 
-            ssteps = max(20, args.steps // 2)
-            sms = time_calls([make_scall(kv) for kv in skv], stream, args.warmup, ssteps) / ssteps
+            ssteps = 100
+            scalls = [make_scall(kv) for kv in skv]
+            warm(scalls, stream, 0.25)
+            sms = time_calls(scalls, stream, 0, ssteps) / ssteps
             sbytes = decode_algorithmic_bytes(scase)
             gbs = sbytes / (sms * 1e-3) / 1e9
             legs[dt] = {"us_per_call": round(sms * 1e3, 2), "GBps": round(gbs, 1),
@@ -611,8 +767,8 @@ def main() -> int:
                 mla.mla_kv_append(new, cu, start, kv, sc, kind, pt_d, pt.shape[1], acase.batch, rows, 64, stream)
 
             asteps = 200
-            # ~20 ms of warm-up calls: the clocks ramp up again after the idle input generation
-            ams = time_calls([acall], stream, 4000, asteps) / asteps
+            warm([acall], stream, 0.25)  # the clocks ramp up again after the idle input generation
+            ams = time_calls([acall], stream, 0, asteps) / asteps
             abytes = rows * (1152 + row_out)  # rows read + rows (and scales) written
             legs[name] = {"us_per_call": round(ams * 1e3, 2), "GBps": round(abytes / (ams * 1e-3) / 1e9, 1),
                           "frac_hbm": round(abytes / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -635,19 +791,8 @@ def main() -> int:
 
     # ---------------- CPU baseline: the oracle ----------------
     if not args.no_cpu_baseline:
-        import oracle
-        cores = max(1, min(16, os.cpu_count() or 1))
         # repeat the whole call until about 10 s of CPU work have run (at most 30 s)
-        runs, cpu_s = 0, 0.0
-        while cpu_s < 10.0 and (runs == 0 or cpu_s / runs * (runs + 1) <= 30.0):
-            t = time.time()
-            oracle.decode(case, nthreads=cores)
-            cpu_s += time.time() - t
-            runs += 1
-        result["cpu_baseline"] = {"value": round(nbytes * runs / cpu_s / 1e9, 4), "unit": "GB/s", "cores": cores,
-                                  "kind": "oracle", "seconds": round(cpu_s, 2), "runs": runs,
-                                  "sample": f"the full {case.name} call (all {T} query tokens x {H} heads), "
-                                            f"fp64 C oracle, {runs} runs"}
+        result["cpu_baseline"] = oracle_decode_baseline(case, nbytes, 10.0)
     result["gpu_clocks"] = {"before": clocks_before, "after": gpu_clocks()}
     print(json.dumps(result))
     return 0

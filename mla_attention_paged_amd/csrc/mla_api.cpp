@@ -34,8 +34,15 @@ DecodePlan plan_decode(int batch, int heads, int q_len, int max_seq_len, int kv_
   // short caches the call is latency-bound, and more, shorter shares plus
   // the merge measured faster than fewer, longer ones (256 rows: 12.3 us
   // with 4 workgroups against 15.9 with 1; 4 x 2K rows: 14.2 against 22.2).
+  //
+  // A block of more than 64 folded rows runs as two row blocks (blockIdx.y), each a
+  // workgroup streaming the same share: the grid then has one workgroup per CU in all,
+  // so that every workgroup is resident at once, and with the share count a multiple
+  // of 8 the two readers of a share land on the same XCD (workgroups are dealt to the
+  // XCDs round-robin by linear index), where the second read of each page hits its L2.
   const long long pages_max = (long long)batch * ceil_div(max_seq_len, kPage);
-  long long g = num_cus > 0 ? num_cus : 1;
+  const int row_blocks = (rows + kBlockRowsHost - 1) / kBlockRowsHost;
+  long long g = num_cus > 0 ? num_cus / row_blocks : 1;
   const long long cap = pages_max;
   if (g > cap) g = cap;
   if (g < 1) g = 1;

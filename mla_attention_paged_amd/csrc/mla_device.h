@@ -81,7 +81,7 @@ constexpr int kI8StageBytes = kI8CodeBytes + kTileRows * 4;  // 18560
 constexpr int kQFrags = kDqk / 32;             // 18 k-steps of 32 features
 constexpr int kOFrags = kDv / 16;              // 32 value-column tiles
 constexpr int kWaves = 8;                      // waves per workgroup (two per SIMD)
-constexpr int kBlockRows = 64;                 // query rows per workgroup
+constexpr int kBlockRows = kBlockRowsHost;     // query rows per workgroup (64)
 constexpr int kOHalf = kOFrags / 2;            // value-column tiles per wave
 
 // Pages of sub * 64 rows are laid out as sub consecutive 64-row sub-pages,

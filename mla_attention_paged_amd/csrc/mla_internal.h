@@ -10,6 +10,7 @@ namespace mla {
 constexpr int kDqk = 576;                      // row width: 512 latent + 64 rope
 constexpr int kDv = 512;                       // value width
 constexpr int kPage = 64;                      // rows per page (= one LDS tile)
+constexpr int kBlockRowsHost = 64;             // folded query rows per decode workgroup
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -114,6 +115,7 @@ PrefillPlan plan_prefill(int batch, int heads, int max_q_len, int total_q, int m
                          int kv_dtype, int num_cus);
 
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream);
+
 hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& g, int heads, hipStream_t stream);

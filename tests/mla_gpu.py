@@ -8,6 +8,16 @@ import mla_attention_paged_amd as mla
 ATOL = 1e-2
 RTOL = 1e-2
 LSE_ATOL = 1e-3
+# Per (token, head) row: ||out - ref|| / ||ref|| over the 512 value columns.  The GPU path
+# rounds three times to bf16 where the fp64 definition does not (the probabilities before
+# the value product, the split-KV partials, the output), each a relative error of at most
+# 2^-8 per element with an RMS of about 2^-8 / sqrt(3); over 512 columns the row ratio
+# concentrates near their combined RMS, about 2^-8.  The bound is four times that.  It is
+# what catches a wrong value path at long lengths, where |ref| ~ 0.02 and the elementwise
+# absolute term alone would pass errors of half the value.
+REL_FROB = 2.0 ** -6
+# rows whose reference norm is below this are left to the elementwise bound
+REL_FROB_MIN_NORM = 1e-3
 
 
 def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
@@ -85,8 +95,15 @@ def assert_close(out, lse, ref_out, ref_lse, what=""):
                                   f" ({int((err > bound).sum())} elements out of tolerance)")
     lerr = np.abs(lse - ref_lse)
     assert (lerr <= LSE_ATOL).all(), f"{what}: lse max error {lerr.max()} at {np.argmax(lerr)}"
-    # diagnostic: relative Frobenius error per (token, head) row
-    rel = np.linalg.norm(out - ref_out, axis=-1) / np.maximum(np.linalg.norm(ref_out, axis=-1), 1e-30)
+    # relative Frobenius error per (token, head) row
+    rnorm = np.linalg.norm(ref_out, axis=-1)
+    rel = np.linalg.norm(out - ref_out, axis=-1) / np.maximum(rnorm, 1e-30)
+    rel = np.where(rnorm >= REL_FROB_MIN_NORM, rel, 0.0)
+    worst_r = np.unravel_index(np.argmax(rel), rel.shape)
+    assert rel.max() <= REL_FROB, (f"{what}: row {worst_r} relative Frobenius error {rel.max():.4g} "
+                                   f"> {REL_FROB:.4g} ({int((rel > REL_FROB).sum())} rows)")
+    print(f"[parity] {what}: max abs err {err.max():.3g}, lse err {lerr.max():.3g}, "
+          f"row rel frob max {rel.max():.3g} mean {rel.mean():.3g}")
     return float(err.max()), float(lerr.max()), float(rel.max())
 
 
@@ -106,3 +123,44 @@ def run_decode_varlen(case, inputs=None, max_q_len=None, stream=None):
                           lse, workspace,
                           workspace.numel(), stream)
     return out, lse
+
+
+def sample_prefill_tokens(case, tok_per_tile: int, rate: float = 1.0 / 32, seed: int = 0):
+    """Query tokens whose rows a sampled parity check compares: the first and last new token
+    of every request, plus one seeded token from each of a seeded ``rate`` share of the work
+    tiles (``tok_per_tile`` consecutive new tokens of one request), so that tiles in the
+    middle of long requests are covered too.  Returns sorted global token indices."""
+    g = np.random.default_rng(seed)
+    cu = case.cu_seqlens_q
+    toks = set()
+    for b in range(case.batch):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi <= lo:
+            continue
+        toks.update((lo, hi - 1))
+        ntiles = (hi - lo + tok_per_tile - 1) // tok_per_tile
+        for t in np.nonzero(g.random(ntiles) < rate)[0]:
+            j0 = lo + int(t) * tok_per_tile
+            toks.add(int(g.integers(j0, min(hi, j0 + tok_per_tile))))
+    return sorted(toks)
+
+
+def permute_pages(cache, seed: int):
+    """The same logical rows at new physical pages (data, scales and page table moved together)."""
+    perm = np.random.default_rng(seed).permutation(cache.num_pages)
+    nd = np.empty_like(cache.data)
+    nd[perm] = cache.data
+    cache.data = nd
+    if cache.scale is not None:
+        ns = np.empty_like(cache.scale)
+        ns[perm] = cache.scale
+        cache.scale = ns
+    cache.page_table = perm[cache.page_table].astype(np.int32)
+    cache.poison_page = int(perm[cache.poison_page])
+    return cache
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a bf16 tensor."""
+    torch.cuda.synchronize()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
