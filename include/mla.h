@@ -95,6 +95,8 @@ extern "C" {
 #define MLA_ERR_UNSUPPORTED 2 /* valid but not implemented: page size, row count, dtype */
 #define MLA_ERR_WORKSPACE 3   /* workspace smaller than mla_splitkv_workspace_size() */
 #define MLA_ERR_HIP 4         /* a HIP runtime call or kernel launch failed */
+#define MLA_ERR_SCRATCH 5     /* mla_decode_noalloc: the split-KV workspace the shape needs
+                                 exceeds MLA_NOALLOC_SCRATCH_BYTES */
 
 /* Cache element types. */
 #define MLA_KV_BF16 0
@@ -110,6 +112,7 @@ extern "C" {
 #define MLA_MAX_PAGE_SIZE 4096 /* largest page size */
 #define MLA_MAX_DECODE_ROWS 128 /* q_len * num_heads of one decode request */
 #define MLA_MAX_HEADS 128   /* prefill: heads of one query token */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20) /* fixed scratch of mla_decode_noalloc, per GPU */
 
 /*
  * Workspace bytes for mla_decode, mla_decode_varlen and mla_prefill_varlen
@@ -317,6 +320,34 @@ int mla_q_absorb(const void* q, const void* w_uk_t, void* q_out, int tokens, int
  * Returns as mla_q_absorb.
  */
 int mla_v_up(const void* o_lat, const void* w_uv, void* out, int tokens, int num_heads, void* hip_stream);
+
+/*
+ * mla_decode without a workspace argument and without any device allocation,
+ * for callers that cannot call hipMalloc: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Arguments, results and
+ * errors are those of mla_decode (the same plan and kernels, so the output is
+ * bitwise the same), except:
+ *
+ *   - the split-KV partials live in a scratch array of MLA_NOALLOC_SCRATCH_BYTES
+ *     (64 MiB) that the library's code object holds on every GPU it is loaded
+ *     on, until the process ends; a shape whose workspace
+ *     (mla_splitkv_workspace_size) exceeds it returns MLA_ERR_SCRATCH before
+ *     anything is enqueued (with 256 compute units: batch <= 764 at
+ *     q_len * num_heads <= 64, batch <= 380 at <= 128);
+ *   - every call on one GPU uses that GPU's one array, which keeps the last
+ *     call's contents: calls that can overlap on one GPU (other streams, or
+ *     other host threads without ordering) race on it and must not be issued.
+ *     Calls ordered on one stream are safe (nothing in the array needs to
+ *     start at zero: each call writes every byte it reads);
+ *   - the first call on a device looks the array's address up (one
+ *     hipGetSymbolAddress per device, with that device current), which may
+ *     not be done while a stream is being captured: make one call, or the
+ *     capture, after a first call outside it.
+ */
+int mla_decode_noalloc(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                       const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens,
+                       int batch, int q_len, int num_heads, int page_size, int max_seq_len,
+                       float softmax_scale, void* out, float* lse, void* hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(int status);

@@ -22,6 +22,8 @@ MLA_ERR_INVALID = 1
 MLA_ERR_UNSUPPORTED = 2
 MLA_ERR_WORKSPACE = 3
 MLA_ERR_HIP = 4
+MLA_ERR_SCRATCH = 5
+MLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 MLA_KV_BF16 = 0
 MLA_KV_INT8 = 1
 MLA_KV_FP8 = 2
@@ -52,6 +54,9 @@ def library():
         lib.mla_decode.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp,
                                    vp, sz, vp]
         lib.mla_decode.restype = i32
+        lib.mla_decode_noalloc.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp,
+                                           vp]
+        lib.mla_decode_noalloc.restype = i32
         lib.mla_decode_varlen.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
                                           vp, vp, vp, sz, vp]
         lib.mla_decode_varlen.restype = i32
@@ -122,6 +127,14 @@ def mla_decode(q, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, s
                               max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                               int(workspace_bytes), _stream(hip_stream))
     _check(rc, "mla_decode")
+
+
+def mla_decode_noalloc(q, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, seq_lens, batch,
+                       q_len, num_heads, page_size, max_seq_len, softmax_scale, out, lse, hip_stream=None) -> None:
+    rc = library().mla_decode_noalloc(_ptr(q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype, _ptr(page_table),
+                                      max_pages_per_req, _ptr(seq_lens), batch, q_len, num_heads, page_size,
+                                      max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _stream(hip_stream))
+    _check(rc, "mla_decode_noalloc")
 
 
 def mla_decode_varlen(q, cu_seqlens_q, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, seq_lens,

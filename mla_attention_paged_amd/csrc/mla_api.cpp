@@ -91,7 +91,8 @@ using namespace mla;
 namespace {
 
 std::mutex g_mu;
-std::map<int, int> g_cus;  // device -> compute units
+constexpr int kMaxDevs = 64;
+int g_cus[kMaxDevs] = {};  // device -> compute units (0: not yet asked)
 std::map<std::tuple<int, int, int, int, int, int>, DecodePlan> g_decode_plans;
 
 // Compute units of the current device (MLA_NUM_CUS overrides, for planning
@@ -106,13 +107,12 @@ int device_cus(int* dev_out, int* cus_out) {
     }
   }
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevs) return MLA_ERR_HIP;
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    auto it = g_cus.find(dev);
-    if (it != g_cus.end()) {
+    if (g_cus[dev] > 0) {
       *dev_out = dev;
-      *cus_out = it->second;
+      *cus_out = g_cus[dev];
       return MLA_OK;
     }
   }
@@ -168,6 +168,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MLA_ERR_WORKSPACE: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime or launch error";
+    case MLA_ERR_SCRATCH: return "split-KV workspace larger than the fixed scratch of mla_decode_noalloc";
     default: return "unknown status";
   }
 }
@@ -220,11 +221,15 @@ namespace {
 
 // Decode with uniform (cu_q null: q_len tokens per request) or per-request
 // query counts (cu_q: device offsets, q_len the largest count, total_q the
-// total).  Host-scalar checks come first, before any HIP call.
+// total).  Host-scalar checks come first, before any HIP call.  With
+// `fixed_scratch`, the workspace arguments are ignored: the plan is computed
+// without the plan cache and the split-KV scratch is the library's fixed device
+// array (MLA_ERR_SCRATCH when the plan needs more).
 int decode_impl(const void* q, const int32_t* cu_q, const void* kv_cache, const float* kv_scale, int kv_dtype,
                 const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens, int batch,
                 int total_q, int q_len, int num_heads, int page_size, int max_seq_len, float softmax_scale,
-                void* out, float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                void* out, float* lse, void* workspace, size_t workspace_bytes, void* hip_stream,
+                bool fixed_scratch = false) {
   if (batch < 1 || q_len < 1 || num_heads < 1 || max_pages_per_req < 1 || max_seq_len < 1)
     return MLA_ERR_INVALID;
   if (total_q < 0 || (long long)total_q > (long long)batch * q_len) return MLA_ERR_INVALID;
@@ -245,10 +250,21 @@ int decode_impl(const void* q, const int32_t* cu_q, const void* kv_cache, const 
   if (total_q == 0) return MLA_OK;  // no query rows: nothing to compute or write
 
   DecodePlan plan{};
-  const int rc = cached_decode_plan(batch, num_heads, q_len, max_seq_len, kv_dtype, &plan);
-  if (rc != MLA_OK) return rc;
-  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
-    return MLA_ERR_WORKSPACE;
+  if (fixed_scratch) {
+    int dev = 0, cus = 0;
+    const int rc = device_cus(&dev, &cus);
+    if (rc != MLA_OK) return rc;
+    plan = plan_decode(batch, num_heads, q_len, max_seq_len, kv_dtype, cus);
+    if (plan.workspace_bytes > kNoAllocScratchBytes) return MLA_ERR_SCRATCH;
+    workspace = nullptr;
+    if (plan.workspace_bytes > 0 && noalloc_scratch(&workspace) != hipSuccess) return MLA_ERR_HIP;
+    workspace_bytes = kNoAllocScratchBytes;
+  } else {
+    const int rc = cached_decode_plan(batch, num_heads, q_len, max_seq_len, kv_dtype, &plan);
+    if (rc != MLA_OK) return rc;
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+      return MLA_ERR_WORKSPACE;
+  }
 
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -290,6 +306,16 @@ int mla_decode(const void* q, const void* kv_cache, const float* kv_scale, int k
   return decode_impl(q, nullptr, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, seq_lens, batch,
                      (int)std::min<long long>((long long)batch * q_len, 0x7fffffffLL), q_len, num_heads,
                      page_size, max_seq_len, softmax_scale, out, lse, workspace, workspace_bytes, hip_stream);
+}
+
+int mla_decode_noalloc(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                       const int32_t* page_table, int max_pages_per_req, const int32_t* seq_lens, int batch,
+                       int q_len, int num_heads, int page_size, int max_seq_len, float softmax_scale, void* out,
+                       float* lse, void* hip_stream) {
+  if (batch < 1 || q_len < 1) return MLA_ERR_INVALID;
+  return decode_impl(q, nullptr, kv_cache, kv_scale, kv_dtype, page_table, max_pages_per_req, seq_lens, batch,
+                     (int)std::min<long long>((long long)batch * q_len, 0x7fffffffLL), q_len, num_heads,
+                     page_size, max_seq_len, softmax_scale, out, lse, nullptr, 0, hip_stream, true);
 }
 
 int mla_decode_varlen(const void* q, const int32_t* cu_seqlens_q, const void* kv_cache, const float* kv_scale,

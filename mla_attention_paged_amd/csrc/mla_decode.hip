@@ -24,6 +24,8 @@
 // The merge then reduces, per request, the partials of the workgroups whose
 // shares intersect it.  Every cache byte is read from HBM once per call,
 // and each page is read by one workgroup for all the request's rows.
+#include <mutex>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -662,6 +664,32 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
     *reinterpret_cast<bf16x4*>(a.out + orow * kDv + col) = h;
     if (quarter == 0 && tid == 0) a.lse[orow] = tot > 0.f ? (m_use + fast_log2(tot)) * kLn2 : -INFINITY;
   }
+}
+
+// Split-KV scratch of the allocation-free decode entry point.  In host code `scratch`
+// names a host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns for the current device is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};  // per device, kept until the process ends
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream) {

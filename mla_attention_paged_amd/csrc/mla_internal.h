@@ -116,6 +116,11 @@ PrefillPlan plan_prefill(int batch, int heads, int max_q_len, int total_q, int m
 
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream);
 
+// The fixed split-KV scratch of mla_decode_noalloc: a device array of this many bytes
+// in the library's code object, one per GPU.  Returns its address on the current device
+// (looked up once per device, with that device current).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& g, int heads, hipStream_t stream);

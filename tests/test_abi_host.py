@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert mla.mla_status_string(code) not in ("", "unknown status")
     assert mla.mla_status_string(99) == "unknown status"
 
@@ -210,3 +210,16 @@ def test_absorb_argument_checks(lib, fn):
     assert f(None, None, None, 0, 16, None) == mla.MLA_OK        # nothing to do, no launch
     assert f(1, 1, 1, 1 << 30, 16, None) == mla.MLA_ERR_UNSUPPORTED
 
+
+def test_noalloc_rejects_plans_beyond_its_scratch(lib):
+    """A shape whose split-KV workspace exceeds the fixed 64 MiB scratch is refused before
+    anything is enqueued (host-only: the plan is computed for 256 compute units)."""
+    wsb = mla.mla_splitkv_workspace_size(4000, 16, 4, 16000, 262144, 0)
+    assert wsb > mla.MLA_NOALLOC_SCRATCH_BYTES
+    rc = lib.mla_decode_noalloc(1, 1, None, 0, 1, 4096, 1, 4000, 4, 16, 64, 262144, 0.07, 1, 1, None)
+    assert rc == mla.MLA_ERR_SCRATCH
+    # the scalar checks of mla_decode come first
+    assert lib.mla_decode_noalloc(None, 1, None, 0, 1, 4096, 1, 4, 4, 16, 64, 262144, 0.07, 1, 1, None) == \
+        mla.MLA_ERR_INVALID
+    assert lib.mla_decode_noalloc(1, 1, None, 0, 1, 4096, 1, 4, 4, 16, 32, 262144, 0.07, 1, 1, None) == \
+        mla.MLA_ERR_UNSUPPORTED
