@@ -120,12 +120,11 @@ constexpr int kPFStages = 4;
 // query rows of a work tile form two 32-row groups rg.  Score wave (rg, kh)
 // holds the query fragments of its group's rows (two 16-row MFMA tiles)
 // and scores them against rows 16kh .. 16kh+15 of each staged tile, so each
-// K fragment read from LDS feeds two MFMAs.  Value wave (rg, ch) holds the
-// accumulators of the same 32 rows for value columns 256ch .. 256ch+255, so
-// each transposed V fragment read feeds two MFMAs.  Per 32-row tile the
-// waves read 74 KB of K and 66 KB of V from LDS, half of what four 16-row
-// groups that each read the whole tile need; the MFMA work per SIMD is the
-// same.
+// K fragment read from LDS feeds two MFMAs.  Value wave vq holds the
+// accumulators of all 64 rows for value columns 128vq .. 128vq+127, so each
+// transposed V fragment read feeds four MFMAs.  Per 32-row tile the waves
+// read 74 KB of K and 33 KB of V from LDS; the MFMA work per SIMD is the
+// same as with any other split.
 //
 // Step k (between barriers B1(k) and B2(k), then B2(k) to B1(k+1)):
 //  - score waves: take the partner's row max of tile k-1 (written after
@@ -137,9 +136,9 @@ constexpr int kPFStages = 4;
 //    latency); after B2(k) they publish tile k's row max;
 //  - value waves: at B1(k) issue every load of tile k + 2 (the score waves
 //    issue none, so they start on their K reads at once); after B2(k),
-//    rescale and run the value product of tile k - 1 from the 32
+//    rescale and run the value product of tile k - 1 from the 16
 //    transposed V fragments in registers, re-reading each fragment from
-//    tile k's stage as soon as its two MFMAs have taken it.
+//    tile k's stage as soon as its four MFMAs have taken it.
 // The V reads of tile k thus overlap the value MFMAs of tile k - 1 and stay
 // out of the score phase: measured, V reads that run into the score waves'
 // K reads slow the whole step, so B1 waits for them.
@@ -214,44 +213,84 @@ __device__ __forceinline__ bf16x4 softmax_half(const f32x4& s, float mx, float& 
   return p;
 }
 
-// The value waves' two parts of a tile's value product: all 32 transposed V
-// fragments of the wave's 256 columns (issued while the score waves work,
-// into 64 registers), then the 32 MFMAs for the two query tiles.
-__device__ __forceinline__ void values_fetch(const MLA_LDS uint8_t* tile, int lane, int ch,
-                                             bf16x4 (&vb)[kOHalf][2]) {
+// The value waves: value wave vq owns value columns 128 vq .. 128 vq + 127
+// (eight 16-column tiles) of all four 16-row query tiles of the 64-row block,
+// so each transposed V fragment read from LDS feeds four MFMAs (a split by
+// 32-row groups and column halves fed two: twice the V bytes read per flop).
+constexpr int kVQTiles = 4;   // 16-row query tiles per value wave
+constexpr int kVCTiles = 8;   // 16-column value tiles per value wave
+
+// Lane's transposed-read address of column tile 0 of quarter vq in a staged tile.
+__device__ __forceinline__ const MLA_LDS uint8_t* vq_base(const MLA_LDS uint8_t* tile, int lane, int vq) {
   const int g = lane >> 4;
   const int i16 = lane & 15;
-  const MLA_LDS uint8_t* vbase = tile + (4 * g + (i16 >> 2)) * kLdsPitch + 4 * (i16 & 3) * 2 + 512 * ch;
+  return tile + (4 * g + (i16 >> 2)) * kLdsPitch + 4 * (i16 & 3) * 2 + 256 * vq;
+}
+
+// All eight V fragments of the wave's quarter of a tile (32 registers).
+__device__ __forceinline__ void values_fetch(const MLA_LDS uint8_t* tile, int lane, int vq,
+                                             bf16x4 (&vb)[kVCTiles][2]) {
+  const MLA_LDS uint8_t* vbase = vq_base(tile, lane, vq);
 #pragma unroll
-  for (int ct = 0; ct < kOHalf; ++ct) {
+  for (int ct = 0; ct < kVCTiles; ++ct) {
     vb[ct][0] = lds_tr16(vbase + 32 * ct);
     vb[ct][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * ct);
   }
 }
 
-// With `next` (the following tile's stage), each column tile's two V
-// fragments are re-read from it as soon as its MFMAs have taken them, so
-// the next tile's V reads overlap this tile's value MFMAs.
+// The value product of the tile in vb for the four query tiles.  With REFILL,
+// each column tile's two V fragments are re-read from `next` (the following
+// tile's stage) as soon as its four MFMAs have taken them, so the next tile's
+// V reads overlap this tile's value MFMAs.
 template <bool REFILL>
-__device__ __forceinline__ void values_mfma(bf16x4 (&vb)[kOHalf][2], bf16x8 p0, bf16x8 p1, f32x4 (&o0)[kOHalf],
-                                            f32x4 (&o1)[kOHalf], const MLA_LDS uint8_t* next, int lane, int ch) {
-  const int g = lane >> 4;
-  const int i16 = lane & 15;
-  const MLA_LDS uint8_t* vbase = next + (4 * g + (i16 >> 2)) * kLdsPitch + 4 * (i16 & 3) * 2 + 512 * ch;
+__device__ __forceinline__ void values_mfma(bf16x4 (&vb)[kVCTiles][2], const bf16x8 (&p)[kVQTiles],
+                                            f32x4 (&o)[kVQTiles][kVCTiles], const MLA_LDS uint8_t* next, int lane,
+                                            int vq) {
+  const MLA_LDS uint8_t* vbase = nullptr;
+  if constexpr (REFILL) vbase = vq_base(next, lane, vq);
 #pragma unroll
-  for (int ct = 0; ct < kOHalf; ++ct) {
+  for (int ct = 0; ct < kVCTiles; ++ct) {
     const bf16x4 v0 = vb[ct][0], v1 = vb[ct][1];
     bf16x8 va;
     va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
     va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
-    o0[ct] = mfma16x16x32(va, p0, o0[ct]);
-    o1[ct] = mfma16x16x32(va, p1, o1[ct]);
+#pragma unroll
+    for (int qt = 0; qt < kVQTiles; ++qt) o[qt][ct] = mfma16x16x32(va, p[qt], o[qt][ct]);
     if constexpr (REFILL) {
       vb[ct][0] = lds_tr16(vbase + 32 * ct);
       vb[ct][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * ct);
     }
   }
 }
+
+// Value waves, after B2: the published probabilities and rescale factors of
+// the four query tiles (query tile qt = 2 row group + tile of the group:
+// entry 64 qt + lane), the rescale when some row's max was raised, then the
+// product.
+template <bool REFILL>
+__device__ __forceinline__ void value_product(const MLA_LDS uint8_t* pb, const MLA_LDS float* al,
+                                              bf16x4 (&vb)[kVCTiles][2], f32x4 (&o)[kVQTiles][kVCTiles],
+                                              const MLA_LDS uint8_t* next, int lane, int vq) {
+  bf16x8 p[kVQTiles];
+  float f[kVQTiles];
+#pragma unroll
+  for (int qt = 0; qt < kVQTiles; ++qt) {
+    p[qt] = *reinterpret_cast<const MLA_LDS bf16x8*>(pb + (64 * qt + lane) * 16);
+    f[qt] = al[64 * qt + lane];
+  }
+  if (__ballot(f[0] != 1.f || f[1] != 1.f || f[2] != 1.f || f[3] != 1.f)) {
+#pragma unroll
+    for (int qt = 0; qt < kVQTiles; ++qt)
+#pragma unroll
+      for (int ct = 0; ct < kVCTiles; ++ct) o[qt][ct] *= f[qt];
+  }
+  values_mfma<REFILL>(vb, p, o, next, lane, vq);
+}
+
+// Value waves, at the end of a work tile: normalise (al holds 1 / row sum) and
+// store the wave's 128 columns of each of the block's rows.
+__device__ __forceinline__ void store_rows(const PrefillArgs& a, const WorkTile& wt, const MLA_LDS float* al,
+                                           const f32x4 (&o)[kVQTiles][kVCTiles], int lane, int vq, int block_rows);
 
 // K prefetch distance (k-steps) of the score waves: the first reads go out
 // before the softmax, which covers their latency.  Measured: 4 ahead beat 6
@@ -280,6 +319,26 @@ __device__ __forceinline__ QRow qrow_of(const PrefillArgs& a, const WorkTile& wt
   return x;
 }
 
+__device__ __forceinline__ void store_rows(const PrefillArgs& a, const WorkTile& wt, const MLA_LDS float* al,
+                                           const f32x4 (&o)[kVQTiles][kVCTiles], int lane, int vq, int block_rows) {
+  const int col = 128 * vq + 4 * (lane >> 4);
+#pragma unroll
+  for (int qt = 0; qt < kVQTiles; ++qt) {
+    const QRow x = qrow_of(a, wt, kBlockRows * wt.rb + 16 * qt + (lane & 15), block_rows);
+    const float inv = al[64 * qt + lane];
+    if (x.ok) {
+      uint16_t* dst = a.out + (size_t)x.qrow * kDv + col;
+#pragma unroll
+      for (int ct = 0; ct < kVCTiles; ++ct) {
+        const f32x4 v = o[qt][ct] * inv;
+        bf16x4 h;
+        h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
+      }
+    }
+  }
+}
+
 struct WsLds {
   MLA_LDS uint8_t* ring;
   MLA_LDS float* mx;     // [4 score waves][2 query tiles][64]: row maxes, then row sums
@@ -293,8 +352,9 @@ struct WsLds {
 template <bool SCORE>
 __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTile& wt, const WsLds& L, int w,
                                              int lane, int block_rows) {
-  const int rg = (w & 3) >> 1;  // row group
-  const int hh = w & 1;         // score waves: tile-row half kh; value waves: column half ch
+  const int rg = (w & 3) >> 1;  // score waves: row group
+  const int hh = w & 1;         // score waves: tile-row half kh
+  const int vq = w & 3;         // value waves: column quarter
   const int g = lane >> 4;
   const int r0 = kBlockRows * wt.rb + 32 * rg + (lane & 15);
   const QRow x0 = qrow_of(a, wt, r0, block_rows), x1 = qrow_of(a, wt, r0 + 16, block_rows);
@@ -320,14 +380,16 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
   float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f, mx0 = -INFINITY, mx1 = -INFINITY;
   f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
   // value-wave state
-  f32x4 o0[kOHalf], o1[kOHalf];
-  bf16x4 vb[kOHalf][2];
+  f32x4 o[kVQTiles][kVCTiles];
+  bf16x4 vb[kVCTiles][2];
   if (SCORE) {
     issue_q(x0.ok ? a.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
     issue_q(x1.ok ? a.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
   } else {
 #pragma unroll
-    for (int i = 0; i < kOHalf; ++i) o0[i] = o1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < kVQTiles; ++qt)
+#pragma unroll
+      for (int ct = 0; ct < kVCTiles; ++ct) o[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // score waves, step k: softmax of the previous tile, then the scores of tile k (kk < 0: none)
@@ -369,17 +431,7 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
   // value waves: the value product of the tile in vb from the published
   // probabilities; with REFILL, vb is re-read from the stage of tile `next`
   auto value_step = [&](auto refill, int next) {
-    const bf16x8 p0 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row);
-    const bf16x8 p1 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row + 64 * 16);
-    const float al0 = al_row[0], al1 = al_row[64];
-    if (__ballot(al0 != 1.f || al1 != 1.f)) {
-#pragma unroll
-      for (int ct = 0; ct < kOHalf; ++ct) {
-        o0[ct] *= al0;
-        o1[ct] *= al1;
-      }
-    }
-    values_mfma<decltype(refill)::value>(vb, p0, p1, o0, o1, stage(next), lane, hh);
+    value_product<decltype(refill)::value>(L.pb, L.al, vb, o, stage(next), lane, vq);
   };
 
   for (int plo = 0; plo < wt.npages; plo += kPWin) {
@@ -438,7 +490,7 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
       mx_mine[0] = mx0;
       mx_mine[64] = mx1;
     } else {
-      values_fetch(stage(0), lane, hh, vb);  // V of tile 0
+      values_fetch(stage(0), lane, vq, vb);  // V of tile 0
     }
     for (int k = 1; k < ntiles; ++k) {
       wait_for(k);
@@ -494,24 +546,7 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
     }
   }
   lds_write_barrier();
-  if (!SCORE) {
-    const float inv0 = al_row[0], inv1 = al_row[64];
-    const int col = (kDv / 2) * hh + 4 * g;
-#pragma unroll
-    for (int jq = 0; jq < 2; ++jq) {
-      const QRow& x = jq == 0 ? x0 : x1;
-      if (x.ok) {
-        uint16_t* dst = a.out + (size_t)x.qrow * kDv + col;
-#pragma unroll
-        for (int ct = 0; ct < kOHalf; ++ct) {
-          const f32x4 v = (jq == 0 ? o0[ct] : o1[ct]) * (jq == 0 ? inv0 : inv1);
-          bf16x4 h;
-          h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
-          *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
-        }
-      }
-    }
-  }
+  if (!SCORE) store_rows(a, wt, L.al, o, lane, vq, block_rows);
 }
 
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws(PrefillArgs a) {
@@ -544,19 +579,23 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws(PrefillA
 
 // ---------------------------------------------------------------------------
 // INT8 / FP8 cache (CODE) on the wave-specialised core (K prefetch depth
-// kKAheadC: the score waves here also hold the row scales).  The codes stream
-// through two LDS code stages; the value waves, whose score-phase work is
-// only the fetch of a tile's V fragments, also convert the next tile's
-// codes to exact bf16 there, into the third of three converted buffers
-// (with the tile's 32 row scales beside it).  Step k:
-//  - B1(k): the codes of tile k + 1 have landed; tile k is converted;
+// kKAheadC: the score waves here also hold the row scales).  The value waves
+// bring each tile's codes straight into registers with ordinary global loads
+// (value thread i: row i / 8 of the tile, 72 consecutive code bytes; thread
+// i < 32 also row i's scale), a step ahead, and widen them to exact bf16
+// into one of three converted tiles in LDS (the tile's 32 row scales beside
+// it) in the value phase, next to their value MFMAs.  No code bytes pass
+// through LDS and no wave issues loads in the score phase.  Step k:
+//  - B1(k): tile k is converted (in step k - 1);
 //  - score waves: softmax of tile k - 1 (probabilities times their row's
 //    scale, selected to 0 on masked rows so that a non-finite scale there
 //    cannot leak; the row sums take the unscaled probabilities), then the
-//    scores of tile k, each row's score times its scale;
-//  - value waves: V fragments of tile k - 1, then tile k + 1's conversion;
-//  - B2(k): tile k + 1's code stage is free: tile k + 3's codes go into it;
-//  - value waves: the value product of tile k - 1.
+//    scores of tile k from its converted tile, each row's score times its
+//    scale; value waves: the V fragments of tile k - 1;
+//  - B2(k): the probabilities of tile k - 1 are published;
+//  - value waves: the value product of tile k - 1, the conversion of tile
+//    k + 1 (its codes were requested in step k - 1) and the loads of tile
+//    k + 2's codes into the registers that just freed up.
 // ---------------------------------------------------------------------------
 
 // mask_half with each tile row's scale (sc: rows 16kh + 4(lane>>4) + e).
@@ -594,10 +633,44 @@ __device__ __forceinline__ bf16x4 softmax_half_sc(const f32x4& s, f32x4 sc, floa
 
 constexpr int kKAheadC = 3;
 
+// One tile's codes in a value thread's registers (see above).
+constexpr int kCodeUnits = kI8RowBytes / 8 / 8;  // 9 units of 8 codes
+
+struct CodeRegs {
+  u32x2 c[kCodeUnits];
+  float sc;  // value threads 0 .. 31: row scale of tile row `thread`
+};
+
+// Request tile `half` (rows 32 half ..) of a page: rows at or past `rem` re-read
+// row 0's codes; their scales are read as they are and never used unmasked.
+__device__ __forceinline__ void load_codes(const uint8_t* __restrict__ page, const float* __restrict__ spage,
+                                           int half, int rem, int vt, CodeRegs& r) {
+  const int t = vt >> 3;
+  const int row = kTileRows * half + t;
+  const uint8_t* src = page + (size_t)(row < rem ? row : 0) * kI8RowBytes + 8 * kCodeUnits * (vt & 7);
+#pragma unroll
+  for (int i = 0; i < kCodeUnits; ++i) r.c[i] = *reinterpret_cast<const u32x2*>(src + 8 * i);
+  r.sc = vt < kTileRows ? spage[kTileRows * half + vt] : 0.f;
+}
+
+// Widen a tile's codes into a converted tile (pitch 1184, like a staged bf16
+// tile) and its scales into `tsc`.
+template <int CODE>
+__device__ __forceinline__ void store_codes(const CodeRegs& r, MLA_LDS uint8_t* cvt, MLA_LDS float* tsc, int vt) {
+  MLA_LDS uint8_t* dst = cvt + (vt >> 3) * kLdsPitch + 16 * kCodeUnits * (vt & 7);
+#pragma unroll
+  for (int i = 0; i < kCodeUnits; ++i) {
+    u32x4 o;
+    o[0] = codepair_to_bf16<CODE, 0>(r.c[i][0]); o[1] = codepair_to_bf16<CODE, 1>(r.c[i][0]);
+    o[2] = codepair_to_bf16<CODE, 0>(r.c[i][1]); o[3] = codepair_to_bf16<CODE, 1>(r.c[i][1]);
+    *reinterpret_cast<MLA_LDS u32x4*>(dst + 16 * i) = o;
+  }
+  if (vt < kTileRows) tsc[vt] = r.sc;
+}
+
 struct WsCodesLds {
-  MLA_LDS uint8_t* codes;  // two code stages
-  MLA_LDS uint8_t* cvt;    // three converted tiles (bf16, pitch 1184)
-  MLA_LDS float* tsc;      // their row scales, 32 each
+  MLA_LDS uint8_t* cvt;  // three converted tiles (bf16, pitch 1184)
+  MLA_LDS float* tsc;    // their row scales, 32 each
   MLA_LDS float* mx;
   MLA_LDS uint8_t* pb;
   MLA_LDS float* al;
@@ -607,15 +680,17 @@ struct WsCodesLds {
 template <bool SCORE, int CODE>
 __device__ __forceinline__ void ws_codes_work_tile(const PrefillArgs& a, const WorkTile& wt, const WsCodesLds& L,
                                                    int w, int lane, int block_rows) {
-  const int rg = (w & 3) >> 1;
-  const int hh = w & 1;
+  const int rg = (w & 3) >> 1;  // score waves: row group
+  const int hh = w & 1;         // score waves: tile-row half kh
+  const int vq = w & 3;         // value waves: column quarter
+  const int vt = threadIdx.x - (kWaves - kLoadWaves) * 64;  // value waves: thread 0 .. 255
   const int g = lane >> 4;
   const int r0 = kBlockRows * wt.rb + 32 * rg + (lane & 15);
   const QRow x0 = qrow_of(a, wt, r0, block_rows), x1 = qrow_of(a, wt, r0 + 16, block_rows);
-  auto code_stage = [&](int k) { return L.codes + (k & 1) * kI8StageBytes; };
   auto cvt_of = [&](int k) { return L.cvt + (k % 3) * kStageBytes; };
+  auto tsc_of = [&](int k) { return L.tsc + (k % 3) * kTileRows; };
   auto tsc4 = [&](int k) {  // this lane's four row scales of tile k (score waves: rows 16kh + 4g + e)
-    return *reinterpret_cast<const MLA_LDS f32x4*>(L.tsc + (k % 3) * kTileRows + 16 * hh + 4 * g);
+    return *reinterpret_cast<const MLA_LDS f32x4*>(tsc_of(k) + 16 * hh + 4 * g);
   };
   MLA_LDS float* const mx_mine = L.mx + 128 * w + lane;
   const MLA_LDS float* const mx_part = L.mx + 128 * (w ^ 1) + lane;
@@ -625,14 +700,17 @@ __device__ __forceinline__ void ws_codes_work_tile(const PrefillArgs& a, const W
   bf16x8 q0[kQFrags], q1[kQFrags];
   float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f, mx0 = -INFINITY, mx1 = -INFINITY;
   f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
-  f32x4 o0[kOHalf], o1[kOHalf];
-  bf16x4 vb[kOHalf][2];
+  f32x4 o[kVQTiles][kVCTiles];
+  bf16x4 vb[kVCTiles][2];
+  CodeRegs rc;  // value waves: the codes of the next tile to convert
   if (SCORE) {
     issue_q(x0.ok ? a.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
     issue_q(x1.ok ? a.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
   } else {
 #pragma unroll
-    for (int i = 0; i < kOHalf; ++i) o0[i] = o1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < kVQTiles; ++qt)
+#pragma unroll
+      for (int ct = 0; ct < kVCTiles; ++ct) o[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   auto score_tile = [&](int kk, int lim0, int lim1) {
@@ -679,100 +757,76 @@ __device__ __forceinline__ void ws_codes_work_tile(const PrefillArgs& a, const W
       mx1 = mask_half_sc(b0 + b1, sc, hh, lim1, a.scale_log2, lane, sp1);
     }
   };
-  auto value_step = [&]() {
-    const bf16x8 p0 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row);
-    const bf16x8 p1 = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_row + 64 * 16);
-    const float al0 = al_row[0], al1 = al_row[64];
-    if (__ballot(al0 != 1.f || al1 != 1.f)) {
-#pragma unroll
-      for (int ct = 0; ct < kOHalf; ++ct) {
-        o0[ct] *= al0;
-        o1[ct] *= al1;
-      }
-    }
-    values_mfma<false>(vb, p0, p1, o0, o1, nullptr, lane, hh);
-  };
-  // value waves: convert tile kk's codes (256 threads)
-  auto convert = [&](int kk) {
-    convert_code_tile_sc<CODE, 4 * 64>(code_stage(kk), cvt_of(kk), L.tsc + (kk % 3) * kTileRows,
-                                       threadIdx.x - 4 * 64);
-  };
 
   for (int plo = 0; plo < wt.npages; plo += kPWin) {
     const int n = min(kPWin, wt.npages - plo);
-    lds_barrier();
+    lds_barrier();  // the previous window's page ids and converted tiles are no longer read
     for (int k = threadIdx.x; k < n; k += kWaves * 64)
       L.pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0);  // the page ids are in LDS
     lds_barrier();
     const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
-    auto issue = [&](int k) {
-      const int p = k >> 1;
-      stage_tile_i8<kWaves>(a.kv + (size_t)L.pid[p] * kI8PageBytes, a.kv_scale + (size_t)L.pid[p] * kPage, k & 1,
-                            wt.kv_end - kPage * (plo + p), code_stage(k), w, lane);
-    };
     auto lim_of = [&](const QRow& x, int k) { return x.ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
-    auto wait_codes = [&](int k) {  // tile k's codes landed; tile k + 1's may stay in flight
-      if (k + 1 < ntiles)
-        wait_tile<kWaves, kI8StageLoads>(1, w);
-      else
-        wait_vmcnt<0>();
+    // tile k's codes (tiles past the window's last re-read the last one, so
+    // that the register sets always hold defined data; they are converted into
+    // a buffer nobody reads)
+    auto load = [&](int k, CodeRegs& r) {
+      if constexpr (!SCORE) {
+        const int kk = min(k, ntiles - 1);
+        const int p = kk >> 1;
+        const int pid = L.pid[p];
+        load_codes(a.kv + (size_t)pid * kI8PageBytes, a.kv_scale + (size_t)pid * kPage, kk & 1,
+                   wt.kv_end - kPage * (plo + p), vt, r);
+      }
     };
-    issue(0);
-    if (1 < ntiles) issue(1);
-    wait_codes(0);
-    lds_write_barrier();  // tile 0's codes landed
-    if (!SCORE) convert(0);
-    lds_write_barrier();  // tile 0 converted, its code stage free
-    if (2 < ntiles) issue(2);
-    // step 0: scores only (and tile 1's conversion)
-    if (1 < ntiles) wait_codes(1);
-    lds_write_barrier();  // B1(0)
-    if (SCORE)
-      score_tile(0, lim_of(x0, 0), lim_of(x1, 0));
-    else if (1 < ntiles)
-      convert(1);
-    lds_write_barrier();  // B2(0)
-    if (3 < ntiles) issue(3);
-    if (SCORE) {
-      mx_mine[0] = mx0;
-      mx_mine[64] = mx1;
-    }
-    for (int k = 1; k < ntiles; ++k) {
-      if (k + 1 < ntiles) wait_codes(k + 1);
-      lds_write_barrier();  // B1(k)
+    auto convert = [&](int k, const CodeRegs& r) {
+      if constexpr (!SCORE) store_codes<CODE>(r, cvt_of(k), tsc_of(k), vt);
+    };
+    auto value_step = [&](auto refill, int next) {
+      value_product<decltype(refill)::value>(L.pb, L.al, vb, o, cvt_of(next), lane, vq);
+    };
+    // steps k >= 1; `rn` holds the codes of tile k + 1
+    auto step = [&](int k, CodeRegs& rn) {
+      lds_write_barrier();  // B1(k): tile k converted
       if (SCORE) {
         score_step(std::true_type{}, k, k - 1, lim_of(x0, k), lim_of(x1, k));
       } else {
-        // the conversion first: the V fragments' 64 registers are not live across it
-        if (k + 1 < ntiles) convert(k + 1);
-        values_fetch(cvt_of(k - 1), lane, hh, vb);
+        convert(k + 1, rn);
+        load(k + 2, rn);
       }
-      lds_write_barrier();  // B2(k): probabilities published, tile k + 1's code stage free
-      if (k + 3 < ntiles) issue(k + 3);
+      lds_write_barrier();  // B2(k): the probabilities of tile k - 1 are published
       if (SCORE) {
         mx_mine[0] = mx0;
         mx_mine[64] = mx1;
       } else {
-        value_step();
+        value_step(std::true_type{}, k);  // tile k - 1, then V of tile k into vb
       }
+    };
+
+    load(0, rc);
+    convert(0, rc);
+    load(1, rc);
+    lds_write_barrier();  // B1(0): tile 0 converted
+    if (SCORE) score_tile(0, lim_of(x0, 0), lim_of(x1, 0));
+    lds_write_barrier();  // B2(0)
+    if (SCORE) {
+      mx_mine[0] = mx0;
+      mx_mine[64] = mx1;
+    } else {
+      convert(1, rc);
+      load(2, rc);
+      values_fetch(cvt_of(0), lane, vq, vb);  // V of tile 0
     }
+    for (int k = 1; k < ntiles; ++k) step(k, rc);
     lds_write_barrier();  // B1'
-    if (SCORE)
-      score_step(std::false_type{}, -1, ntiles - 1, 0, 0);
-    else
-      values_fetch(cvt_of(ntiles - 1), lane, hh, vb);
-    if (SCORE)
-      lds_write_barrier();  // B2'
-    else
-      lds_barrier();
-    if (!SCORE) value_step();
+    if (SCORE) score_step(std::false_type{}, -1, ntiles - 1, 0, 0);
+    lds_write_barrier();  // B2'
+    if (!SCORE) value_step(std::false_type{}, 0);
   }
 
   lds_write_barrier();
   float s0 = 0.f, s1 = 0.f;
   if (SCORE) {
-    wait_vmcnt<0>();
     s0 = wave_sum_rows(l0);
     s1 = wave_sum_rows(l1);
     mx_mine[0] = s0;
@@ -791,38 +845,20 @@ __device__ __forceinline__ void ws_codes_work_tile(const PrefillArgs& a, const W
     }
   }
   lds_write_barrier();
-  if (!SCORE) {
-    const float inv0 = al_row[0], inv1 = al_row[64];
-    const int col = (kDv / 2) * hh + 4 * g;
-#pragma unroll
-    for (int jq = 0; jq < 2; ++jq) {
-      const QRow& x = jq == 0 ? x0 : x1;
-      if (x.ok) {
-        uint16_t* dst = a.out + (size_t)x.qrow * kDv + col;
-#pragma unroll
-        for (int ct = 0; ct < kOHalf; ++ct) {
-          const f32x4 v = (jq == 0 ? o0[ct] : o1[ct]) * (jq == 0 ? inv0 : inv1);
-          bf16x4 h;
-          h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
-          *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
-        }
-      }
-    }
-  }
+  if (!SCORE) store_rows(a, wt, L.al, o, lane, vq, block_rows);
 }
 
 template <int CODE>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws_codes(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[3 * kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t codes_raw[2 * kI8StageBytes];
   __shared__ __attribute__((aligned(16))) float tsc_raw[3 * kTileRows];
   __shared__ __attribute__((aligned(16))) float mx_raw[4 * 2 * 64];
   __shared__ __attribute__((aligned(16))) uint8_t pb_raw[2 * 2 * 64 * 16];
   __shared__ __attribute__((aligned(16))) float al_raw[2 * 2 * 64];
   __shared__ int s_pid[kPWin];
   __shared__ int s_tile;
-  const WsCodesLds L{(MLA_LDS uint8_t*)codes_raw, (MLA_LDS uint8_t*)cvt_raw, (MLA_LDS float*)tsc_raw,
-                     (MLA_LDS float*)mx_raw,      (MLA_LDS uint8_t*)pb_raw,  (MLA_LDS float*)al_raw, s_pid};
+  const WsCodesLds L{(MLA_LDS uint8_t*)cvt_raw, (MLA_LDS float*)tsc_raw, (MLA_LDS float*)mx_raw,
+                     (MLA_LDS uint8_t*)pb_raw, (MLA_LDS float*)al_raw, s_pid};
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int total_tiles = a.tile_cum[a.batch];
