@@ -28,6 +28,7 @@
 
 #include "mla_device.h"
 #include "mla_internal.h"
+#include "mla_ws.h"
 
 namespace mla {
 
@@ -401,147 +402,68 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   }
 }
 
-// Phase one for an INT8 or FP8 cache (CODE), software-pipelined like the
-// bf16 kernel.  The codes stream through three LDS stages (two tiles in
-// flight: a code tile is half the bytes of a bf16 one); step t of a window
-// waits for the codes of tile t, passes barrier A (every wave is done with
-// step t - 1), starts tile t + 2, converts tile t to exact bf16 in one of two
-// converted buffers (its 32 row scales beside it), passes barrier C, then
-// computes the scores of tile t from its converted buffer while the softmax
-// and value product of tile t - 1 use the other buffer and its scales.  The
-// score halves travel between partner waves through a double-buffered slot,
-// so two barriers per step suffice.
-constexpr int kCStages = 3;
-
+// Phase one for an INT8 or FP8 cache (CODE) on the wave-specialised core of
+// the prefill kernels (mla_ws.h): score waves and value waves, the codes
+// loaded into the value waves' registers and widened to bf16 while the score
+// waves compute, the V fragments read behind the value MFMAs.  Workgroup g
+// walks its share of the page stream one request segment at a time: the
+// request's folded rows (row block blockIdx.y) against the share's pages of
+// that request, written as the partial of slot g + b (or, with a single
+// workgroup, as the final output).  The merge is the bf16 decode's.
 template <int CODE>
-__global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_codes(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t codes_raw[kCStages * kI8StageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[2 * kStageBytes];
-  __shared__ __attribute__((aligned(16))) float tsc_raw[2 * kTileRows];
-  __shared__ __attribute__((aligned(16))) f32x4 xchg_raw[2 * kWaves * 64];
-  MLA_LDS uint8_t* const codes = (MLA_LDS uint8_t*)codes_raw;
-  MLA_LDS uint8_t* const cvt = (MLA_LDS uint8_t*)cvt_raw;
-  MLA_LDS float* const tsc = (MLA_LDS float*)tsc_raw;
-  MLA_LDS f32x4* const xchg = (MLA_LDS f32x4*)xchg_raw;
-  __shared__ int s_pid[2 * kWin], s_req[2 * kWin], s_rem[2 * kWin];
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_ws_codes(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t cvt_raw[3 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) float tsc_raw[3 * kTileRows];
+  __shared__ __attribute__((aligned(16))) float mx_raw[4 * 2 * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t pb_raw[2 * 2 * 64 * 16];
+  __shared__ __attribute__((aligned(16))) float al_raw[2 * 2 * 64];
+  __shared__ int s_pid[kPWin];
   __shared__ int s_info[5];
   __shared__ int s_len[kLenCache];
   __shared__ int s_tok[kLenCache + 1];
-
+  const WsCodesLds L{(MLA_LDS uint8_t*)cvt_raw, (MLA_LDS float*)tsc_raw, (MLA_LDS float*)mx_raw,
+                     (MLA_LDS uint8_t*)pb_raw, (MLA_LDS float*)al_raw, s_pid};
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = blockIdx.x;
   if (w == 0) locate_share(a, g, lane, s_info, s_len, s_tok);
   __syncthreads();
   const Lens lens{a, s_len};
-  const int seg_lo = s_info[0], seg_hi = s_info[1];
-  if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
-  int cb = s_info[2], cj = s_info[3];
-
-  const int half = w >> 2;
-  const int row = kBlockRows * blockIdx.y + 16 * (w & 3) + (lane & 15);
-  const bool wave_rows = kBlockRows * blockIdx.y + 16 * (w & 3) < a.rows;
-  // the current request's query rows: this lane's row exists when
-  // row < n * heads, and its token (row / heads) sees rows t <= L - late
-  bool row_ok = false;
-  int late = 0, tok0 = 0;
-  auto set_req = [&](int b) {
+  const WsArgs wa{a.kv, a.kv_scale, a.page_table, a.pt_stride, a.sub, a.scale_log2};
+  int left = s_info[1] - s_info[0];  // pages of the share
+  int j = s_info[3];                 // first page of the share in its first request
+  for (int b = s_info[2]; left > 0 && b < a.batch; ++b, j = 0) {
+    const int L_b = lens(b);
+    const int take = min(left, (L_b + kPage - 1) / kPage - j);
+    if (take <= 0) continue;
+    left -= take;
     const ReqQ r = req_q(a, s_tok, b);
-    row_ok = row < r.n * a.heads;
-    late = r.n - (row_ok ? row / a.heads : 0);
-    tok0 = r.tok0;
-  };
-  MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
-  MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
-  auto code_stage = [&](int t) { return codes + (t % kCStages) * kI8StageBytes; };
-  auto cvt_of = [&](int t) { return cvt + (t & 1) * kStageBytes; };
-  auto tsc_of = [&](int t) { return tsc + (t & 1) * kTileRows; };
-
-  RowState st;
-  bf16x8 qf[kQFrags];
-  int cur_b = -1;
-  int q_b = -1;  // request whose query fragments are loaded or in flight
-  if (wave_rows && cb < a.batch) {
-    set_req(cb);
-    issue_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
-    q_b = cb;
-  }
-
-  for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
-    const int n = min(kWin, seg_hi - wlo);
-    __syncthreads();  // the previous window's list, stages and buffers are no longer read
-    fill_window_tiles(a, lens, n, cb, cj, s_pid, s_req, s_rem, &s_info[4], w, lane);
-    __syncthreads();
-    const int N = s_info[4];
-    auto issue = [&](int t) {
-      stage_tile_i8<kWaves>(a.kv + (size_t)s_pid[t] * kI8PageBytes, a.kv_scale + (size_t)s_pid[t] * kPage,
-                            s_req[t] & 1, s_rem[t] + kTileRows * (s_req[t] & 1), code_stage(t), w, lane);
-    };
-    issue(0);
-    if (N > 1) issue(1);
-    int issued = N > 1 ? 2 : 1;
-    auto wait_for = [&](int t) {  // codes of tile t landed; tile t + 1 may stay in flight
-      if (t + 1 < issued) wait_tile<kWaves, kI8StageLoads>(1, w); else wait_vmcnt<0>();
-    };
-    // steps up to barrier C: tile t's codes in, tile t + 2 started, tile t converted
-    auto bring = [&](int t) {
-      wait_for(t);
-      lds_write_barrier();  // A: codes of t visible; every wave is done with step t - 1
-      if (issued < N) {
-        issue(issued);
-        ++issued;
-      }
-      convert_code_tile_sc<CODE>(code_stage(t), cvt_of(t), tsc_of(t), threadIdx.x);
-      lds_write_barrier();  // C: tile t converted
-    };
-    for (int t0 = 0; t0 < N;) {
-      const int b = s_req[t0] >> 1;
-      int t1 = t0 + 1;
-      while (t1 < N && (s_req[t1] >> 1) == b) ++t1;
-      if (wave_rows && b != cur_b) {
-        if (cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
-        set_req(b);
-        if (b != q_b) load_q(row_ok ? a.q + ((size_t)tok0 * a.heads + row) * kDqk : nullptr, lane, qf);
-        q_b = -1;
-        reset_state(st);
-      }
-      cur_b = b;
-      // first step: scores only
-      bring(t0);
-      f32x4 s_prev = {0.f, 0.f, 0.f, 0.f};
-      if (wave_rows) {
-        s_prev = tile_scores(cvt_of(t0), qf, lane, half);
-        xmine[(t0 & 1) * kWaves * 64] = s_prev;
-      }
-      int prev_lim = s_rem[t0] - late;
-      for (int t = t0 + 1; t < t1; ++t) {
-        bring(t);
-        const int lim = s_rem[t] - late;
-        if (wave_rows) {
-          const f32x4 other = xpart[((t - 1) & 1) * kWaves * 64];
-          const f32x4 lo = half == 0 ? s_prev : other;
-          const f32x4 hi = half == 0 ? other : s_prev;
-          s_prev = tile_step<true>(cvt_of(t), cvt_of(t - 1), qf, lo, hi, prev_lim, a.scale_log2, lane, half, st,
-                                   tsc_of(t - 1));
-          xmine[(t & 1) * kWaves * 64] = s_prev;
-        }
-        prev_lim = lim;
-      }
-      // last tile of the segment
-      lds_write_barrier();
-      if (wave_rows) {
-        const f32x4 other = xpart[((t1 - 1) & 1) * kWaves * 64];
-        const f32x4 lo = half == 0 ? s_prev : other;
-        const f32x4 hi = half == 0 ? other : s_prev;
-        float alpha;
-        const bf16x8 pb = tile_softmax<true>(lo, hi, prev_lim, a.scale_log2, lane, st, alpha, tsc_of(t1 - 1));
-        rescale_o(st, alpha);
-        tile_values(cvt_of(t1 - 1), pb, lane, half, st);
-      }
-      t0 = t1;
+    WsBlock k;
+    k.q = a.q + (size_t)r.tok0 * a.heads * kDqk;
+    if (a.grid == 1) {
+      k.out = a.out + (size_t)r.tok0 * a.heads * kDv;
+      k.lse = a.lse + (size_t)r.tok0 * a.heads;
+      k.lse_mul = kLn2;
+    } else {
+      k.out = a.part_o + (size_t)(g + b) * a.rows * kDv;
+      k.lse = a.part_lse + (size_t)(g + b) * a.rows;
+      k.lse_mul = 1.f;  // partial log-sum-exp in log2 units, as the merge reads it
     }
+    k.r0 = kBlockRows * blockIdx.y;
+    k.nrows = r.n * a.heads;
+    k.vis0 = L_b - r.n;
+    k.heads = a.heads;
+    k.b = b;
+    k.p_lo = j;
+    k.p_hi = j + take;
+    k.kv_end = L_b;
+    if (k.r0 >= k.nrows) continue;  // this row block has no rows of the request
+    __syncthreads();                // the previous segment is done with the LDS
+    if (w < 4)
+      ws_codes_range<true, CODE>(wa, k, L, w, lane);
+    else
+      ws_codes_range<false, CODE>(wa, k, L, w, lane);
   }
-  if (wave_rows && cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
 }
 
 // Phase two: per (request, row), reduce the partials of the workgroups
@@ -695,11 +617,9 @@ hipError_t noalloc_scratch(void** ptr) {
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int kv_dtype, hipStream_t stream) {
   const int row_blocks = (args.rows + kBlockRows - 1) / kBlockRows;
   if (kv_dtype == 1)
-    hipLaunchKernelGGL(decode_phase1_codes<kCodeInt8>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream,
-                       args);
+    hipLaunchKernelGGL(decode_ws_codes<kCodeInt8>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   else if (kv_dtype == 2)
-    hipLaunchKernelGGL(decode_phase1_codes<kCodeFp8>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream,
-                       args);
+    hipLaunchKernelGGL(decode_ws_codes<kCodeFp8>, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   else
     hipLaunchKernelGGL(decode_phase1_pipe, dim3(plan.grid, row_blocks), dim3(kWaves * 64), 0, stream, args);
   hipError_t e = hipGetLastError();

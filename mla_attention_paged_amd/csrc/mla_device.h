@@ -4,11 +4,11 @@
 // attends a block of up to 64 query rows against the cache, which it
 // streams through a ring of LDS stages of 32 cache rows (half a page) each
 // (three stages in the bf16 decode kernel, four in the bf16 prefill kernel,
-// code stages plus converted buffers in the INT8 / FP8 kernels).  In the
-// decode kernels, waves w and w + 4 share the 16 query rows 16 (w % 4) ..
-// +15 and split the work of each tile in two halves, h = w / 4 (the prefill
-// kernels specialise their waves instead: score waves and value waves on
-// 32-row groups, in mla_prefill.hip):
+// three converted tiles in the INT8 / FP8 kernels).  In the bf16 decode
+// kernel, waves w and w + 4 share the 16 query rows 16 (w % 4) .. +15 and
+// split the work of each tile in two halves, h = w / 4 (the prefill kernels
+// and the INT8 / FP8 decode kernel specialise their waves instead: score
+// waves and value waves, in mla_ws.h):
 //
 //   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over the 576 features: A = 16
 //                   cache rows (rows 16h .. 16h + 15 of the tile) read from
@@ -68,16 +68,11 @@ constexpr int kStageLoads = kTileSlots / 64;            // 37 wave-wide loads pe
 static_assert(kStageLoads * 64 == kTileSlots, "a tile is a whole number of wave-wide loads");
 constexpr int kStageBytes = kStageLoads * 1024;         // 37888
 
-// INT8 / FP8 cache: a stage holds the 32 rows' codes (576 B each, unpadded: they
-// are only read by the conversion pass, 16 contiguous bytes per lane) and
-// their 32 fp32 scales.  Codes are half the bytes of a bf16 row, so the ring
-// is deeper (five tiles in flight) to keep as many bytes in flight.
+// INT8 / FP8 cache: a row is 576 one-byte codes (and one fp32 scale beside the
+// page); a 32-row tile of codes is 18,432 contiguous bytes of its page.
 constexpr int kI8RowBytes = kDqk;                          // 576
 constexpr int kI8PageBytes = kPage * kI8RowBytes;          // 36864
-constexpr int kI8CodeBytes = kTileRows * kI8RowBytes;      // 18432: 18 wave-wide loads
-constexpr int kI8CodeLoads = kI8CodeBytes / 1024;
-constexpr int kI8StageLoads = kI8CodeLoads + 1;            // + one 8-lane load of the scales
-constexpr int kI8StageBytes = kI8CodeBytes + kTileRows * 4;  // 18560
+constexpr int kI8CodeBytes = kTileRows * kI8RowBytes;      // 18432
 constexpr int kQFrags = kDqk / 32;             // 18 k-steps of 32 features
 constexpr int kOFrags = kDv / 16;              // 32 value-column tiles
 constexpr int kWaves = 8;                      // waves per workgroup (two per SIMD)
@@ -213,30 +208,6 @@ __device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ page, int
   }
 }
 
-// INT8 / FP8 tile staging: loads 0..17 bring the 32 rows' codes (16-byte chunk s
-// of the tile is row s / 36, bytes 16 (s % 36) ..), load 18 brings the 32
-// scales with lanes 0..7.  Rows at or past `rem` re-read row 0's codes; their
-// scales are fetched as they are and never used unmasked.
-template <int NW>
-__device__ __forceinline__ void stage_tile_i8(const uint8_t* __restrict__ page, const float* __restrict__ spage,
-                                              int half, int rem, MLA_LDS uint8_t* stage, int wave, int lane) {
-#pragma unroll
-  for (int i0 = 0; i0 < kI8StageLoads; i0 += NW) {
-    const int i = i0 + wave;
-    if (i < kI8CodeLoads) {
-      const int sl = i * 64 + lane;
-      const int t = sl / 36;
-      const int row = kTileRows * half + t;
-      const int src = (row < rem ? row : 0) * kI8RowBytes + (sl - t * 36) * 16;
-      lds_dma16(page, src, stage + i * 1024);
-    } else if (i == kI8CodeLoads) {
-      if (lane < kTileRows / 4)
-        lds_dma16(reinterpret_cast<const uint8_t*>(spage), (kTileRows * half + 4 * lane) * 4,
-                  stage + kI8CodeBytes);
-    }
-  }
-}
-
 // Two signed int8 codes (bytes 2k, 2k+1 of x) as two exact bf16 values.
 __device__ __forceinline__ unsigned i8pair_to_bf16(unsigned x, int k) {
   const float f0 = (float)(int)(signed char)(x >> (16 * k));
@@ -263,50 +234,6 @@ constexpr int kCodeFp8 = 2;
 template <int CODE, int K>
 __device__ __forceinline__ unsigned codepair_to_bf16(unsigned x) {
   return CODE == kCodeFp8 ? fp8pair_to_bf16<K>(x) : i8pair_to_bf16(x, K);
-}
-
-// Convert a staged tile's codes (INT8 or E4M3) into exact bf16 values in
-// `cvt`, laid out like a staged bf16 tile (pitch 1184), cooperatively by
-// kThreads threads (the workgroup's, by default).  The unit is 8 codes (8
-// bytes in, 16 bytes out): thread i converts units i, i + kThreads, ... of
-// the 2304, all of whose loads are issued before the first conversion (one
-// LDS round trip), and consecutive lanes read and write consecutive slots,
-// so neither side has bank conflicts (16 codes per lane written as two
-// 16-byte halves 32 bytes apart conflicted 8 ways).
-template <int CODE, int kThreads = kWaves * 64>
-__device__ __forceinline__ void convert_code_tile(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt, int tid) {
-  constexpr int kUnits = kI8CodeBytes / 8;  // 2304
-  constexpr int kPer = (kUnits + kThreads - 1) / kThreads;
-  constexpr int kRowUnits = kI8RowBytes / 8;  // 72
-  static_assert(kUnits > (kPer - 1) * kThreads, "only the last round of units is partial");
-  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-  u32x2_t x[kPer];
-  constexpr bool kEven = kUnits % kThreads == 0;  // then no lane needs a bounds test
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (kEven || i < kPer - 1 || tid + i * kThreads < kUnits)
-      x[i] = *reinterpret_cast<const MLA_LDS u32x2_t*>(stage + 8 * (tid + i * kThreads));
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int u = tid + i * kThreads;
-    if (kEven || i < kPer - 1 || u < kUnits) {
-      const int t = u / kRowUnits, j = u - kRowUnits * t;
-      u32x4 o;
-      o[0] = codepair_to_bf16<CODE, 0>(x[i][0]); o[1] = codepair_to_bf16<CODE, 1>(x[i][0]);
-      o[2] = codepair_to_bf16<CODE, 0>(x[i][1]); o[3] = codepair_to_bf16<CODE, 1>(x[i][1]);
-      *reinterpret_cast<MLA_LDS u32x4*>(cvt + t * kLdsPitch + 16 * j) = o;
-    }
-  }
-}
-
-// The same, and the tile's 32 row scales copied to `tsc` (for the pipelined
-// core, which reads a tile's scales one step after its codes are gone).
-template <int CODE, int kThreads = kWaves * 64>
-__device__ __forceinline__ void convert_code_tile_sc(const MLA_LDS uint8_t* stage, MLA_LDS uint8_t* cvt,
-                                                     MLA_LDS float* tsc, int tid) {
-  convert_code_tile<CODE, kThreads>(stage, cvt, tid);
-  if (tid < kTileRows / 4)
-    reinterpret_cast<MLA_LDS f32x4*>(tsc)[tid] = reinterpret_cast<const MLA_LDS f32x4*>(stage + kI8CodeBytes)[tid];
 }
 
 // Per-wave attention state: 16 query rows x 256 value columns.
@@ -447,26 +374,15 @@ __device__ __forceinline__ f32x4 tile_scores(const MLA_LDS uint8_t* tile, const 
 // one branch-free block that can be interleaved with the next tile's score
 // MFMAs.  Returns the probabilities in the B-operand layout of the value
 // product.
-template <bool SCALED = false>
 __device__ __forceinline__ bf16x8 tile_softmax(f32x4 lo, f32x4 hi, int lim, float scale_log2, int lane,
-                                               RowState& st, float& alpha, const MLA_LDS float* tsc = nullptr) {
+                                               RowState& st, float& alpha) {
   const int g = lane >> 4;
-  f32x4 sc_lo = {1.f, 1.f, 1.f, 1.f}, sc_hi = {1.f, 1.f, 1.f, 1.f};
-  if (SCALED) {
-    sc_lo = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 4 * g);
-    sc_hi = *reinterpret_cast<const MLA_LDS f32x4*>(tsc + 16 + 4 * g);
-  }
   float s[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    float v0 = lo[e] * scale_log2, v1 = hi[e] * scale_log2;
-    if (SCALED) {
-      v0 *= sc_lo[e];
-      v1 *= sc_hi[e];
-    }
-    v0 = 4 * g + e <= lim ? v0 : -INFINITY;
-    v1 = 16 + 4 * g + e <= lim ? v1 : -INFINITY;
+    const float v0 = 4 * g + e <= lim ? lo[e] * scale_log2 : -INFINITY;
+    const float v1 = 16 + 4 * g + e <= lim ? hi[e] * scale_log2 : -INFINITY;
     s[e] = v0;
     s[4 + e] = v1;
     mx = fmaxf(mx, fmaxf(v0, v1));
@@ -485,19 +401,8 @@ __device__ __forceinline__ bf16x8 tile_softmax(f32x4 lo, f32x4 hi, int lim, floa
   }
   st.l = st.l * alpha + psum;
   bf16x8 pb;
-  if (SCALED) {
-    // the row sum takes the unscaled probabilities; the value product the
-    // probability times the row's scale (a select on masked rows, whose scale
-    // may be non-finite)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pb[e] = (__bf16)(4 * g + e <= lim ? s[e] * sc_lo[e] : 0.f);
-      pb[4 + e] = (__bf16)(16 + 4 * g + e <= lim ? s[4 + e] * sc_hi[e] : 0.f);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
-  }
+  for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[e];
   return pb;
 }
 
@@ -543,14 +448,12 @@ __device__ __forceinline__ void tile_values(const MLA_LDS uint8_t* tile, bf16x8 
 // softmax of tile k-1 interleaved into the MFMA chain, then the value
 // product of tile k-1.  Scores and softmax are independent and in one
 // basic block, so the VALU work can issue while the MFMAs execute.
-template <bool SCALED = false>
 __device__ __forceinline__ f32x4 tile_step(const MLA_LDS uint8_t* tile_k, const MLA_LDS uint8_t* tile_prev,
                                            const bf16x8 (&qf)[kQFrags], f32x4 lo, f32x4 hi, int lim,
-                                           float scale_log2, int lane, int half, RowState& st,
-                                           const MLA_LDS float* tsc_prev = nullptr) {
+                                           float scale_log2, int lane, int half, RowState& st) {
   const f32x4 sc = tile_scores(tile_k, qf, lane, half);
   float alpha;
-  const bf16x8 pb = tile_softmax<SCALED>(lo, hi, lim, scale_log2, lane, st, alpha, tsc_prev);
+  const bf16x8 pb = tile_softmax(lo, hi, lim, scale_log2, lane, st, alpha);
   rescale_o(st, alpha);
   tile_values(tile_prev, pb, lane, half, st);
   return sc;

@@ -24,10 +24,9 @@
 
 #include "mla_device.h"
 #include "mla_internal.h"
+#include "mla_ws.h"
 
 namespace mla {
-
-constexpr int kPWin = 256;  // page ids staged per window (a pipeline restart per window)
 
 __device__ __forceinline__ int p_clamp(int L, int max_pages) {
   L = L < 0 ? 0 : L;
@@ -83,6 +82,32 @@ __global__ __launch_bounds__(256) void prefill_worklist(PrefillArgs a) {
 struct WorkTile {
   int b, q0, j0, j1, P_b, kv_end, npages, rb;
 };
+
+__device__ __forceinline__ WorkTile locate_work(const PrefillArgs& a, int t, int row_blocks);
+
+// The work tile's block: its tokens' rows from the first, the pages its
+// last token sees, outputs in place.
+__device__ __forceinline__ WsBlock block_of(const PrefillArgs& a, const WorkTile& wt) {
+  WsBlock k;
+  const size_t row0 = (size_t)(wt.q0 + wt.j0) * a.heads;  // the tile's first query row
+  k.q = a.q + row0 * kDqk;
+  k.out = a.out + row0 * kDv;
+  k.lse = a.lse + row0;
+  k.lse_mul = kLn2;
+  k.r0 = kBlockRows * wt.rb;
+  k.nrows = (wt.j1 - wt.j0) * a.heads;
+  k.vis0 = wt.P_b + wt.j0;
+  k.heads = a.heads;
+  k.b = wt.b;
+  k.p_lo = 0;
+  k.p_hi = wt.npages;
+  k.kv_end = wt.kv_end;
+  return k;
+}
+
+__device__ __forceinline__ WsArgs ws_args(const PrefillArgs& a) {
+  return WsArgs{a.kv, a.kv_scale, a.page_table, a.pt_stride, a.sub, a.scale_log2};
+}
 
 __device__ __forceinline__ WorkTile locate_work(const PrefillArgs& a, int t, int row_blocks) {
   // order position k with tile_cum[k] <= t < tile_cum[k+1]
@@ -148,196 +173,10 @@ constexpr int kPFStages = 4;
 // and k + 2 load.
 // ---------------------------------------------------------------------------
 
-// Scores of this wave's 16 tile rows against two 16-row query tiles: each K
-// fragment is read once and used by both tiles' MFMAs (four accumulator
-// chains).  s_j[e]: tile row 16kh + 4(lane>>4) + e, query row lane & 15 of
-// query tile j.
-__device__ __forceinline__ void scores_2q(const MLA_LDS uint8_t* tile, const bf16x8 (&q0)[kQFrags],
-                                          const bf16x8 (&q1)[kQFrags], int lane, int kh, f32x4& s0, f32x4& s1) {
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const MLA_LDS uint8_t* kbase = tile + tile_off(16 * kh + r16, g);
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
-  bf16x8 kb[kKDepth + 1];
-#pragma unroll
-  for (int d = 0; d < kKDepth; ++d) kb[d] = lds_b128(kbase + 64 * d);
-#pragma unroll
-  for (int ks = 0; ks < kQFrags; ++ks) {
-    if (ks + kKDepth < kQFrags) kb[(ks + kKDepth) % (kKDepth + 1)] = lds_b128(kbase + 64 * (ks + kKDepth));
-    const bf16x8 kf = kb[ks % (kKDepth + 1)];
-    if (ks & 1) {
-      a1 = mfma16x16x32(kf, q0[ks], a1);
-      b1 = mfma16x16x32(kf, q1[ks], b1);
-    } else {
-      a0 = mfma16x16x32(kf, q0[ks], a0);
-      b0 = mfma16x16x32(kf, q1[ks], b0);
-    }
-  }
-  s0 = a0 + a1;
-  s1 = b0 + b1;
-}
-
-// Scale to log2 units and mask (tile row tt visible when tt <= lim); returns
-// the row max over the wave's 16 tile rows (equal on the row's four lanes).
-__device__ __forceinline__ float mask_half(f32x4 acc, int kh, int lim, float scale_log2, int lane, f32x4& s) {
-  const int g = lane >> 4;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float v = 16 * kh + 4 * g + e <= lim ? acc[e] * scale_log2 : -INFINITY;
-    s[e] = v;
-    mx = fmaxf(mx, v);
-  }
-  return wave_max_rows(mx);
-}
-
-// Online softmax of this wave's 16 rows of a tile, given the row max over
-// all 32 (mx): raises the running max m past the slack, returns the four
-// probabilities (bf16, the wave's half of the value product's B operand)
-// and the factor alpha for the accumulators; lh is this lane's share of the
-// row sum over the wave's rows of every tile.
-__device__ __forceinline__ bf16x4 softmax_half(const f32x4& s, float mx, float& m, float& lh, float& alpha) {
-  const float m_new = mx > m + kRescaleSlack ? mx : m;
-  alpha = m_new == m ? 1.f : fast_exp2(m - m_new);
-  m = m_new;
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  bf16x4 p;
-  float ps = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float v = fast_exp2(s[e] - m_use);
-    ps += v;
-    p[e] = (__bf16)v;
-  }
-  lh = lh * alpha + ps;
-  return p;
-}
-
-// The value waves: value wave vq owns value columns 128 vq .. 128 vq + 127
-// (eight 16-column tiles) of all four 16-row query tiles of the 64-row block,
-// so each transposed V fragment read from LDS feeds four MFMAs (a split by
-// 32-row groups and column halves fed two: twice the V bytes read per flop).
-constexpr int kVQTiles = 4;   // 16-row query tiles per value wave
-constexpr int kVCTiles = 8;   // 16-column value tiles per value wave
-
-// Lane's transposed-read address of column tile 0 of quarter vq in a staged tile.
-__device__ __forceinline__ const MLA_LDS uint8_t* vq_base(const MLA_LDS uint8_t* tile, int lane, int vq) {
-  const int g = lane >> 4;
-  const int i16 = lane & 15;
-  return tile + (4 * g + (i16 >> 2)) * kLdsPitch + 4 * (i16 & 3) * 2 + 256 * vq;
-}
-
-// All eight V fragments of the wave's quarter of a tile (32 registers).
-__device__ __forceinline__ void values_fetch(const MLA_LDS uint8_t* tile, int lane, int vq,
-                                             bf16x4 (&vb)[kVCTiles][2]) {
-  const MLA_LDS uint8_t* vbase = vq_base(tile, lane, vq);
-#pragma unroll
-  for (int ct = 0; ct < kVCTiles; ++ct) {
-    vb[ct][0] = lds_tr16(vbase + 32 * ct);
-    vb[ct][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * ct);
-  }
-}
-
-// The value product of the tile in vb for the four query tiles.  With REFILL,
-// each column tile's two V fragments are re-read from `next` (the following
-// tile's stage) as soon as its four MFMAs have taken them, so the next tile's
-// V reads overlap this tile's value MFMAs.
-template <bool REFILL>
-__device__ __forceinline__ void values_mfma(bf16x4 (&vb)[kVCTiles][2], const bf16x8 (&p)[kVQTiles],
-                                            f32x4 (&o)[kVQTiles][kVCTiles], const MLA_LDS uint8_t* next, int lane,
-                                            int vq) {
-  const MLA_LDS uint8_t* vbase = nullptr;
-  if constexpr (REFILL) vbase = vq_base(next, lane, vq);
-#pragma unroll
-  for (int ct = 0; ct < kVCTiles; ++ct) {
-    const bf16x4 v0 = vb[ct][0], v1 = vb[ct][1];
-    bf16x8 va;
-    va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
-    va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
-#pragma unroll
-    for (int qt = 0; qt < kVQTiles; ++qt) o[qt][ct] = mfma16x16x32(va, p[qt], o[qt][ct]);
-    if constexpr (REFILL) {
-      vb[ct][0] = lds_tr16(vbase + 32 * ct);
-      vb[ct][1] = lds_tr16(vbase + 16 * kLdsPitch + 32 * ct);
-    }
-  }
-}
-
-// Value waves, after B2: the published probabilities and rescale factors of
-// the four query tiles (query tile qt = 2 row group + tile of the group:
-// entry 64 qt + lane), the rescale when some row's max was raised, then the
-// product.
-template <bool REFILL>
-__device__ __forceinline__ void value_product(const MLA_LDS uint8_t* pb, const MLA_LDS float* al,
-                                              bf16x4 (&vb)[kVCTiles][2], f32x4 (&o)[kVQTiles][kVCTiles],
-                                              const MLA_LDS uint8_t* next, int lane, int vq) {
-  bf16x8 p[kVQTiles];
-  float f[kVQTiles];
-#pragma unroll
-  for (int qt = 0; qt < kVQTiles; ++qt) {
-    p[qt] = *reinterpret_cast<const MLA_LDS bf16x8*>(pb + (64 * qt + lane) * 16);
-    f[qt] = al[64 * qt + lane];
-  }
-  if (__ballot(f[0] != 1.f || f[1] != 1.f || f[2] != 1.f || f[3] != 1.f)) {
-#pragma unroll
-    for (int qt = 0; qt < kVQTiles; ++qt)
-#pragma unroll
-      for (int ct = 0; ct < kVCTiles; ++ct) o[qt][ct] *= f[qt];
-  }
-  values_mfma<REFILL>(vb, p, o, next, lane, vq);
-}
-
-// Value waves, at the end of a work tile: normalise (al holds 1 / row sum) and
-// store the wave's 128 columns of each of the block's rows.
-__device__ __forceinline__ void store_rows(const PrefillArgs& a, const WorkTile& wt, const MLA_LDS float* al,
-                                           const f32x4 (&o)[kVQTiles][kVCTiles], int lane, int vq, int block_rows);
-
 // K prefetch distance (k-steps) of the score waves: the first reads go out
 // before the softmax, which covers their latency.  Measured: 4 ahead beat 6
 // by 2% and 6 beat 8 (alternating runs on one box).
 constexpr int kKAhead = 4;
-
-// Waves that issue the bf16 tile loads (the value waves, the last four).
-constexpr int kLoadWaves = 4;
-
-// A query row of a work tile: row r of the tile is head r % heads of token
-// j0 + r / heads.
-struct QRow {
-  bool ok;       // the row exists
-  int qrow;      // its index in [total_q * heads]
-  int vis_last;  // last cache row its token sees
-};
-
-__device__ __forceinline__ QRow qrow_of(const PrefillArgs& a, const WorkTile& wt, int r, int block_rows) {
-  QRow x;
-  const int tok = r / a.heads;
-  const int head = r - tok * a.heads;
-  const int j = wt.j0 + tok;
-  x.ok = r < block_rows && j < wt.j1;
-  x.qrow = (wt.q0 + j) * a.heads + head;
-  x.vis_last = wt.P_b + j;
-  return x;
-}
-
-__device__ __forceinline__ void store_rows(const PrefillArgs& a, const WorkTile& wt, const MLA_LDS float* al,
-                                           const f32x4 (&o)[kVQTiles][kVCTiles], int lane, int vq, int block_rows) {
-  const int col = 128 * vq + 4 * (lane >> 4);
-#pragma unroll
-  for (int qt = 0; qt < kVQTiles; ++qt) {
-    const QRow x = qrow_of(a, wt, kBlockRows * wt.rb + 16 * qt + (lane & 15), block_rows);
-    const float inv = al[64 * qt + lane];
-    if (x.ok) {
-      uint16_t* dst = a.out + (size_t)x.qrow * kDv + col;
-#pragma unroll
-      for (int ct = 0; ct < kVCTiles; ++ct) {
-        const f32x4 v = o[qt][ct] * inv;
-        bf16x4 h;
-        h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
-        *reinterpret_cast<bf16x4*>(dst + 16 * ct) = h;
-      }
-    }
-  }
-}
 
 struct WsLds {
   MLA_LDS uint8_t* ring;
@@ -350,14 +189,13 @@ struct WsLds {
 // One work tile, as a score wave (SCORE) or a value wave.  Both kinds pass
 // the same barriers in the same order; each keeps only its own state live.
 template <bool SCORE>
-__device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTile& wt, const WsLds& L, int w,
-                                             int lane, int block_rows) {
+__device__ __forceinline__ void ws_work_tile(const WsArgs& a, const WsBlock& k_, const WsLds& L, int w, int lane) {
   const int rg = (w & 3) >> 1;  // score waves: row group
   const int hh = w & 1;         // score waves: tile-row half kh
   const int vq = w & 3;         // value waves: column quarter
   const int g = lane >> 4;
-  const int r0 = kBlockRows * wt.rb + 32 * rg + (lane & 15);
-  const QRow x0 = qrow_of(a, wt, r0, block_rows), x1 = qrow_of(a, wt, r0 + 16, block_rows);
+  const int r0 = 32 * rg + (lane & 15);
+  const QRow x0 = ws_row(k_, r0), x1 = ws_row(k_, r0 + 16);
   auto stage = [&](int k) { return L.ring + (k % kPFStages) * kStageBytes; };
   MLA_LDS float* const mx_mine = L.mx + 128 * w + lane;
   const MLA_LDS float* const mx_part = L.mx + 128 * (w ^ 1) + lane;
@@ -383,8 +221,8 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
   f32x4 o[kVQTiles][kVCTiles];
   bf16x4 vb[kVCTiles][2];
   if (SCORE) {
-    issue_q(x0.ok ? a.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
-    issue_q(x1.ok ? a.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
+    issue_q(x0.ok ? k_.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
+    issue_q(x1.ok ? k_.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
   } else {
 #pragma unroll
     for (int qt = 0; qt < kVQTiles; ++qt)
@@ -434,14 +272,14 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
     value_product<decltype(refill)::value>(L.pb, L.al, vb, o, stage(next), lane, vq);
   };
 
-  for (int plo = 0; plo < wt.npages; plo += kPWin) {
-    const int n = min(kPWin, wt.npages - plo);
+  for (int plo = k_.p_lo; plo < k_.p_hi; plo += kPWin) {
+    const int n = min(kPWin, k_.p_hi - plo);
     lds_barrier();  // the previous window's list and stages are no longer read
     for (int k = threadIdx.x; k < n; k += kWaves * 64)
-      L.pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
+      L.pid[k] = sub_page(a.page_table, (size_t)k_.b * a.pt_stride, plo + k, a.sub);
     __builtin_amdgcn_s_waitcnt(0);  // the page ids are in LDS (and every earlier load has landed)
     lds_barrier();
-    const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
+    const int ntiles = min(2 * n, (k_.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
     // Only the value waves issue tile loads (kLoadWaves of them), so the
     // score waves start each step on their K reads; the page id of the next
     // tile to issue is read from LDS one step ahead.
@@ -449,7 +287,7 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
     auto issue = [&](int k, int pid) {
       const int p = k >> 1;
       const int half = k & 1;
-      const int rem = wt.kv_end - kPage * (plo + p);
+      const int rem = k_.kv_end - kPage * (plo + p);
       const uint8_t* page = a.kv + (size_t)pid * kPageBytes;
       if (rem >= kTileRows * (half + 1)) {  // every row of the tile is the request's
         const uint8_t* hbase = page + (size_t)half * kTileRows * kRowBytes;
@@ -540,13 +378,13 @@ __device__ __forceinline__ void ws_work_tile(const PrefillArgs& a, const WorkTil
       al_row[0] = t0 > 0.f ? 1.0f / t0 : 0.f;
       al_row[64] = t1 > 0.f ? 1.0f / t1 : 0.f;
       if (g == 0) {
-        if (x0.ok) a.lse[x0.qrow] = t0 > 0.f ? (m0 + fast_log2(t0)) * kLn2 : -INFINITY;
-        if (x1.ok) a.lse[x1.qrow] = t1 > 0.f ? (m1 + fast_log2(t1)) * kLn2 : -INFINITY;
+        if (x0.ok) k_.lse[x0.qrow] = t0 > 0.f ? (m0 + fast_log2(t0)) * k_.lse_mul : -INFINITY;
+        if (x1.ok) k_.lse[x1.qrow] = t1 > 0.f ? (m1 + fast_log2(t1)) * k_.lse_mul : -INFINITY;
       }
     }
   }
   lds_write_barrier();
-  if (!SCORE) store_rows(a, wt, L.al, o, lane, vq, block_rows);
+  if (!SCORE) ws_store_rows(k_, L.al, o, lane, vq);
 }
 
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws(PrefillArgs a) {
@@ -569,283 +407,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws(PrefillA
     __syncthreads();
     const int t = s_tile;
     if (t >= total_tiles) break;
-    const WorkTile wt = locate_work(a, t, row_blocks);
+    const WsBlock k = block_of(a, locate_work(a, t, row_blocks));
     if (w < 4)
-      ws_work_tile<true>(a, wt, L, w, lane, block_rows);
+      ws_work_tile<true>(ws_args(a), k, L, w, lane);
     else
-      ws_work_tile<false>(a, wt, L, w, lane, block_rows);
+      ws_work_tile<false>(ws_args(a), k, L, w, lane);
   }
-}
-
-// ---------------------------------------------------------------------------
-// INT8 / FP8 cache (CODE) on the wave-specialised core (K prefetch depth
-// kKAheadC: the score waves here also hold the row scales).  The value waves
-// bring each tile's codes straight into registers with ordinary global loads
-// (value thread i: row i / 8 of the tile, 72 consecutive code bytes; thread
-// i < 32 also row i's scale), a step ahead, and widen them to exact bf16
-// into one of three converted tiles in LDS (the tile's 32 row scales beside
-// it) in the value phase, next to their value MFMAs.  No code bytes pass
-// through LDS and no wave issues loads in the score phase.  Step k:
-//  - B1(k): tile k is converted (in step k - 1);
-//  - score waves: softmax of tile k - 1 (probabilities times their row's
-//    scale, selected to 0 on masked rows so that a non-finite scale there
-//    cannot leak; the row sums take the unscaled probabilities), then the
-//    scores of tile k from its converted tile, each row's score times its
-//    scale; value waves: the V fragments of tile k - 1;
-//  - B2(k): the probabilities of tile k - 1 are published;
-//  - value waves: the value product of tile k - 1, the conversion of tile
-//    k + 1 (its codes were requested in step k - 1) and the loads of tile
-//    k + 2's codes into the registers that just freed up.
-// ---------------------------------------------------------------------------
-
-// mask_half with each tile row's scale (sc: rows 16kh + 4(lane>>4) + e).
-__device__ __forceinline__ float mask_half_sc(f32x4 acc, f32x4 sc, int kh, int lim, float scale_log2, int lane,
-                                              f32x4& s) {
-  const int g = lane >> 4;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float v = 16 * kh + 4 * g + e <= lim ? acc[e] * scale_log2 * sc[e] : -INFINITY;
-    s[e] = v;
-    mx = fmaxf(mx, v);
-  }
-  return wave_max_rows(mx);
-}
-
-// softmax_half whose published probabilities carry their row's scale.
-__device__ __forceinline__ bf16x4 softmax_half_sc(const f32x4& s, f32x4 sc, float mx, float& m, float& lh,
-                                                  float& alpha) {
-  const float m_new = mx > m + kRescaleSlack ? mx : m;
-  alpha = m_new == m ? 1.f : fast_exp2(m - m_new);
-  m = m_new;
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  bf16x4 p;
-  float ps = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float v = fast_exp2(s[e] - m_use);
-    ps += v;
-    p[e] = (__bf16)(s[e] == -INFINITY ? 0.f : v * sc[e]);
-  }
-  lh = lh * alpha + ps;
-  return p;
-}
-
-constexpr int kKAheadC = 3;
-
-// One tile's codes in a value thread's registers (see above).
-constexpr int kCodeUnits = kI8RowBytes / 8 / 8;  // 9 units of 8 codes
-
-struct CodeRegs {
-  u32x2 c[kCodeUnits];
-  float sc;  // value threads 0 .. 31: row scale of tile row `thread`
-};
-
-// Request tile `half` (rows 32 half ..) of a page: rows at or past `rem` re-read
-// row 0's codes; their scales are read as they are and never used unmasked.
-__device__ __forceinline__ void load_codes(const uint8_t* __restrict__ page, const float* __restrict__ spage,
-                                           int half, int rem, int vt, CodeRegs& r) {
-  const int t = vt >> 3;
-  const int row = kTileRows * half + t;
-  const uint8_t* src = page + (size_t)(row < rem ? row : 0) * kI8RowBytes + 8 * kCodeUnits * (vt & 7);
-#pragma unroll
-  for (int i = 0; i < kCodeUnits; ++i) r.c[i] = *reinterpret_cast<const u32x2*>(src + 8 * i);
-  r.sc = vt < kTileRows ? spage[kTileRows * half + vt] : 0.f;
-}
-
-// Widen a tile's codes into a converted tile (pitch 1184, like a staged bf16
-// tile) and its scales into `tsc`.
-template <int CODE>
-__device__ __forceinline__ void store_codes(const CodeRegs& r, MLA_LDS uint8_t* cvt, MLA_LDS float* tsc, int vt) {
-  MLA_LDS uint8_t* dst = cvt + (vt >> 3) * kLdsPitch + 16 * kCodeUnits * (vt & 7);
-#pragma unroll
-  for (int i = 0; i < kCodeUnits; ++i) {
-    u32x4 o;
-    o[0] = codepair_to_bf16<CODE, 0>(r.c[i][0]); o[1] = codepair_to_bf16<CODE, 1>(r.c[i][0]);
-    o[2] = codepair_to_bf16<CODE, 0>(r.c[i][1]); o[3] = codepair_to_bf16<CODE, 1>(r.c[i][1]);
-    *reinterpret_cast<MLA_LDS u32x4*>(dst + 16 * i) = o;
-  }
-  if (vt < kTileRows) tsc[vt] = r.sc;
-}
-
-struct WsCodesLds {
-  MLA_LDS uint8_t* cvt;  // three converted tiles (bf16, pitch 1184)
-  MLA_LDS float* tsc;    // their row scales, 32 each
-  MLA_LDS float* mx;
-  MLA_LDS uint8_t* pb;
-  MLA_LDS float* al;
-  int* pid;
-};
-
-template <bool SCORE, int CODE>
-__device__ __forceinline__ void ws_codes_work_tile(const PrefillArgs& a, const WorkTile& wt, const WsCodesLds& L,
-                                                   int w, int lane, int block_rows) {
-  const int rg = (w & 3) >> 1;  // score waves: row group
-  const int hh = w & 1;         // score waves: tile-row half kh
-  const int vq = w & 3;         // value waves: column quarter
-  const int vt = threadIdx.x - (kWaves - kLoadWaves) * 64;  // value waves: thread 0 .. 255
-  const int g = lane >> 4;
-  const int r0 = kBlockRows * wt.rb + 32 * rg + (lane & 15);
-  const QRow x0 = qrow_of(a, wt, r0, block_rows), x1 = qrow_of(a, wt, r0 + 16, block_rows);
-  auto cvt_of = [&](int k) { return L.cvt + (k % 3) * kStageBytes; };
-  auto tsc_of = [&](int k) { return L.tsc + (k % 3) * kTileRows; };
-  auto tsc4 = [&](int k) {  // this lane's four row scales of tile k (score waves: rows 16kh + 4g + e)
-    return *reinterpret_cast<const MLA_LDS f32x4*>(tsc_of(k) + 16 * hh + 4 * g);
-  };
-  MLA_LDS float* const mx_mine = L.mx + 128 * w + lane;
-  const MLA_LDS float* const mx_part = L.mx + 128 * (w ^ 1) + lane;
-  MLA_LDS uint8_t* const pb_row = L.pb + (128 * rg + lane) * 16;
-  MLA_LDS float* const al_row = L.al + 128 * rg + lane;
-
-  bf16x8 q0[kQFrags], q1[kQFrags];
-  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f, mx0 = -INFINITY, mx1 = -INFINITY;
-  f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
-  f32x4 o[kVQTiles][kVCTiles];
-  bf16x4 vb[kVCTiles][2];
-  CodeRegs rc;  // value waves: the codes of the next tile to convert
-  if (SCORE) {
-    issue_q(x0.ok ? a.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
-    issue_q(x1.ok ? a.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
-  } else {
-#pragma unroll
-    for (int qt = 0; qt < kVQTiles; ++qt)
-#pragma unroll
-      for (int ct = 0; ct < kVCTiles; ++ct) o[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  auto score_tile = [&](int kk, int lim0, int lim1) {
-    f32x4 c0, c1;
-    scores_2q(cvt_of(kk), q0, q1, lane, hh, c0, c1);
-    const f32x4 sc = tsc4(kk);
-    mx0 = mask_half_sc(c0, sc, hh, lim0, a.scale_log2, lane, sp0);
-    mx1 = mask_half_sc(c1, sc, hh, lim1, a.scale_log2, lane, sp1);
-  };
-  // score waves, step kk: softmax of tile kprev, then (with_scores) the scores of tile kk
-  auto score_step = [&](auto with_scores, int kk, int kprev, int lim0, int lim1) {
-    constexpr bool kScores = decltype(with_scores)::value;
-    const MLA_LDS uint8_t* kbase = cvt_of(kk < 0 ? 0 : kk) + tile_off(16 * hh + (lane & 15), g);
-    bf16x8 kb[kKAheadC];
-    if constexpr (kScores) {
-#pragma unroll
-      for (int d = 0; d < kKAheadC; ++d) kb[d] = lds_b128(kbase + 64 * d);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // the first K reads go out before the softmax
-    const f32x4 scp = tsc4(kprev);
-    float al0, al1;
-    const bf16x4 p0 = softmax_half_sc(sp0, scp, fmaxf(mx0, mx_part[0]), m0, l0, al0);
-    const bf16x4 p1 = softmax_half_sc(sp1, scp, fmaxf(mx1, mx_part[64]), m1, l1, al1);
-    *reinterpret_cast<MLA_LDS bf16x4*>(pb_row + 8 * hh) = p0;
-    *reinterpret_cast<MLA_LDS bf16x4*>(pb_row + 64 * 16 + 8 * hh) = p1;
-    al_row[0] = al0;
-    al_row[64] = al1;
-    if constexpr (kScores) {
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
-#pragma unroll
-      for (int ks = 0; ks < kQFrags; ++ks) {
-        const bf16x8 kf = kb[ks % kKAheadC];
-        if (ks + kKAheadC < kQFrags) kb[ks % kKAheadC] = lds_b128(kbase + 64 * (ks + kKAheadC));
-        if (ks & 1) {
-          a1 = mfma16x16x32(kf, q0[ks], a1);
-          b1 = mfma16x16x32(kf, q1[ks], b1);
-        } else {
-          a0 = mfma16x16x32(kf, q0[ks], a0);
-          b0 = mfma16x16x32(kf, q1[ks], b0);
-        }
-      }
-      const f32x4 sc = tsc4(kk);
-      mx0 = mask_half_sc(a0 + a1, sc, hh, lim0, a.scale_log2, lane, sp0);
-      mx1 = mask_half_sc(b0 + b1, sc, hh, lim1, a.scale_log2, lane, sp1);
-    }
-  };
-
-  for (int plo = 0; plo < wt.npages; plo += kPWin) {
-    const int n = min(kPWin, wt.npages - plo);
-    lds_barrier();  // the previous window's page ids and converted tiles are no longer read
-    for (int k = threadIdx.x; k < n; k += kWaves * 64)
-      L.pid[k] = sub_page(a.page_table, (size_t)wt.b * a.pt_stride, plo + k, a.sub);
-    __builtin_amdgcn_s_waitcnt(0);  // the page ids are in LDS
-    lds_barrier();
-    const int ntiles = min(2 * n, (wt.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
-    auto lim_of = [&](const QRow& x, int k) { return x.ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
-    // tile k's codes (tiles past the window's last re-read the last one, so
-    // that the register sets always hold defined data; they are converted into
-    // a buffer nobody reads)
-    auto load = [&](int k, CodeRegs& r) {
-      if constexpr (!SCORE) {
-        const int kk = min(k, ntiles - 1);
-        const int p = kk >> 1;
-        const int pid = L.pid[p];
-        load_codes(a.kv + (size_t)pid * kI8PageBytes, a.kv_scale + (size_t)pid * kPage, kk & 1,
-                   wt.kv_end - kPage * (plo + p), vt, r);
-      }
-    };
-    auto convert = [&](int k, const CodeRegs& r) {
-      if constexpr (!SCORE) store_codes<CODE>(r, cvt_of(k), tsc_of(k), vt);
-    };
-    auto value_step = [&](auto refill, int next) {
-      value_product<decltype(refill)::value>(L.pb, L.al, vb, o, cvt_of(next), lane, vq);
-    };
-    // steps k >= 1; `rn` holds the codes of tile k + 1
-    auto step = [&](int k, CodeRegs& rn) {
-      lds_write_barrier();  // B1(k): tile k converted
-      if (SCORE) {
-        score_step(std::true_type{}, k, k - 1, lim_of(x0, k), lim_of(x1, k));
-      } else {
-        convert(k + 1, rn);
-        load(k + 2, rn);
-      }
-      lds_write_barrier();  // B2(k): the probabilities of tile k - 1 are published
-      if (SCORE) {
-        mx_mine[0] = mx0;
-        mx_mine[64] = mx1;
-      } else {
-        value_step(std::true_type{}, k);  // tile k - 1, then V of tile k into vb
-      }
-    };
-
-    load(0, rc);
-    convert(0, rc);
-    load(1, rc);
-    lds_write_barrier();  // B1(0): tile 0 converted
-    if (SCORE) score_tile(0, lim_of(x0, 0), lim_of(x1, 0));
-    lds_write_barrier();  // B2(0)
-    if (SCORE) {
-      mx_mine[0] = mx0;
-      mx_mine[64] = mx1;
-    } else {
-      convert(1, rc);
-      load(2, rc);
-      values_fetch(cvt_of(0), lane, vq, vb);  // V of tile 0
-    }
-    for (int k = 1; k < ntiles; ++k) step(k, rc);
-    lds_write_barrier();  // B1'
-    if (SCORE) score_step(std::false_type{}, -1, ntiles - 1, 0, 0);
-    lds_write_barrier();  // B2'
-    if (!SCORE) value_step(std::false_type{}, 0);
-  }
-
-  lds_write_barrier();
-  float s0 = 0.f, s1 = 0.f;
-  if (SCORE) {
-    s0 = wave_sum_rows(l0);
-    s1 = wave_sum_rows(l1);
-    mx_mine[0] = s0;
-    mx_mine[64] = s1;
-  }
-  lds_write_barrier();
-  if (SCORE) {
-    const float t0 = s0 + mx_part[0], t1 = s1 + mx_part[64];
-    if (hh == 0) {
-      al_row[0] = t0 > 0.f ? 1.0f / t0 : 0.f;
-      al_row[64] = t1 > 0.f ? 1.0f / t1 : 0.f;
-      if (g == 0) {
-        if (x0.ok) a.lse[x0.qrow] = t0 > 0.f ? (m0 + fast_log2(t0)) * kLn2 : -INFINITY;
-        if (x1.ok) a.lse[x1.qrow] = t1 > 0.f ? (m1 + fast_log2(t1)) * kLn2 : -INFINITY;
-      }
-    }
-  }
-  lds_write_barrier();
-  if (!SCORE) store_rows(a, wt, L.al, o, lane, vq, block_rows);
 }
 
 template <int CODE>
@@ -870,11 +437,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws_codes(Pr
     __syncthreads();
     const int t = s_tile;
     if (t >= total_tiles) break;
-    const WorkTile wt = locate_work(a, t, row_blocks);
+    const WsBlock k = block_of(a, locate_work(a, t, row_blocks));
     if (w < 4)
-      ws_codes_work_tile<true, CODE>(a, wt, L, w, lane, block_rows);
+      ws_codes_range<true, CODE>(ws_args(a), k, L, w, lane);
     else
-      ws_codes_work_tile<false, CODE>(a, wt, L, w, lane, block_rows);
+      ws_codes_range<false, CODE>(ws_args(a), k, L, w, lane);
   }
 }
 

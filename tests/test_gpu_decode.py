@@ -382,3 +382,22 @@ def test_decode_workload2_sampled():
     ref_out, ref_lse = oracle.decode(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
     errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, case.name)
     print("workload2 sampled: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)
+
+
+def test_decode_fp8_nan_code_tail_has_no_effect():
+    """Rows past each request's end (and the poison page) hold the E4M3 NaN code 0x7F with a
+    NaN scale: the output must equal the run with finite poison bit for bit."""
+    lens = [70, 129, 1, 4000]
+    a = synth.make_decode_case(529, 4, 16, 1, seq_lens=lens, max_seq_len=4096, kv_dtype="fp8")
+    b = synth.make_decode_case(529, 4, 16, 1, seq_lens=lens, max_seq_len=4096, kv_dtype="fp8")
+    c = b.cache
+    for bb, L in enumerate(lens):
+        n = (L + 63) // 64
+        c.data[c.page_table[bb, n - 1], L - 64 * (n - 1):] = 0x7F
+        c.scale[c.page_table[bb, n - 1], L - 64 * (n - 1):] = np.float32("nan")
+    c.data[c.poison_page] = 0x7F
+    oa, la = run_decode(a)
+    ob, lb = run_decode(b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)) and torch.equal(la, lb)
+    assert torch.isfinite(ob.float()).all()

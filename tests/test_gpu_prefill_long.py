@@ -165,3 +165,21 @@ def test_prefill_long_matches_oracle_all_tokens():
     out, lse = host(*run_prefill(case))
     ref_out, ref_lse = oracle.prefill(case, nthreads=NT)
     assert_close(out, lse, ref_out, ref_lse, "prefixes across the window edge")
+
+
+def test_prefill_fp8_nan_code_tail_has_no_effect():
+    """FP8 prefill: rows past each request's end hold the E4M3 NaN code 0x7F with a NaN
+    scale; the output must equal the run with finite poison bit for bit."""
+    kw = dict(prefix_lens=[WIN + 5, 300], new_lens=[33, 7], kv_dtype="fp8")
+    a = synth.make_prefill_case(605, 16, **kw)
+    b = synth.make_prefill_case(605, 16, **kw)
+    c = b.cache
+    for bb, L in enumerate(c.kv_lens):
+        n = (int(L) + 63) // 64
+        c.data[c.page_table[bb, n - 1], int(L) - 64 * (n - 1):] = 0x7F
+        c.scale[c.page_table[bb, n - 1], int(L) - 64 * (n - 1):] = np.float32("nan")
+    oa, la = run_prefill(a)
+    ob, lb = run_prefill(b)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(oa), bits(ob)) and torch.equal(la, lb)
+    assert torch.isfinite(ob.float()).all()
