@@ -424,16 +424,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_ws_codes(DecodeArgs a) 
   const WsCodesLds L{(MLA_LDS uint8_t*)cvt_raw, (MLA_LDS float*)tsc_raw, (MLA_LDS float*)mx_raw,
                      (MLA_LDS uint8_t*)pb_raw, (MLA_LDS float*)al_raw, s_pid};
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = wave_uniform(threadIdx.x >> 6);
   const int g = blockIdx.x;
   if (w == 0) locate_share(a, g, lane, s_info, s_len, s_tok);
   __syncthreads();
   const Lens lens{a, s_len};
   const WsArgs wa{a.kv, a.kv_scale, a.page_table, a.pt_stride, a.sub, a.scale_log2};
-  int left = s_info[1] - s_info[0];  // pages of the share
-  int j = s_info[3];                 // first page of the share in its first request
-  for (int b = s_info[2]; left > 0 && b < a.batch; ++b, j = 0) {
-    const int L_b = lens(b);
+  int left = wave_uniform(s_info[1] - s_info[0]);  // pages of the share
+  int j = wave_uniform(s_info[3]);                 // first page of the share in its first request
+  for (int b = wave_uniform(s_info[2]); left > 0 && b < a.batch; ++b, j = 0) {
+    const int L_b = wave_uniform(lens(b));
     const int take = min(left, (L_b + kPage - 1) / kPage - j);
     if (take <= 0) continue;
     left -= take;
@@ -459,10 +459,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_ws_codes(DecodeArgs a) 
     k.kv_end = L_b;
     if (k.r0 >= k.nrows) continue;  // this row block has no rows of the request
     __syncthreads();                // the previous segment is done with the LDS
+    const WsBlock ku = wave_uniform(k);
     if (w < 4)
-      ws_codes_range<true, CODE>(wa, k, L, w, lane);
+      ws_codes_range<true, CODE>(wa, ku, L, w, lane);
     else
-      ws_codes_range<false, CODE>(wa, k, L, w, lane);
+      ws_codes_range<false, CODE>(wa, ku, L, w, lane);
   }
 }
 

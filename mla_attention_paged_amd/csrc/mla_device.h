@@ -216,15 +216,16 @@ __device__ __forceinline__ unsigned i8pair_to_bf16(unsigned x, int k) {
   return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
 }
 
-// Two E4M3 codes (bytes 2k, 2k+1 of x) as two exact bf16 values: gfx950's
-// packed FP8 -> fp32 conversion (it decodes the OCP E4M3 format: checked on
-// the GPU against every code byte), then the upper halves of the two fp32
-// values, which are exact bf16 (E4M3 values have 4 significant bits).
-typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+// Two E4M3 codes (bytes 2k, 2k+1 of x) as two exact bf16 values, in one
+// gfx950 scaled FP8 -> bf16 conversion with scale 1 (it decodes the OCP E4M3
+// format; every code byte is checked on the GPU through both attention
+// kernels).  E4M3 values have 4 significant bits and exponents inside bf16's
+// normal range, so the result is exact.
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
 template <int K>
 __device__ __forceinline__ unsigned fp8pair_to_bf16(unsigned x) {
-  const f32x2_cvt f = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, K != 0);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  const bf16x2_cvt b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, K != 0);
+  return __builtin_bit_cast(unsigned, b);
 }
 
 // Cache code formats of the scaled caches.

@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws_codes(Pr
   const WsCodesLds L{(MLA_LDS uint8_t*)cvt_raw, (MLA_LDS float*)tsc_raw, (MLA_LDS float*)mx_raw,
                      (MLA_LDS uint8_t*)pb_raw, (MLA_LDS float*)al_raw, s_pid};
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = wave_uniform(threadIdx.x >> 6);
   const int total_tiles = a.tile_cum[a.batch];
   const int block_rows = a.tok_per_tile * a.heads;
   const int row_blocks = (block_rows + kBlockRows - 1) / kBlockRows;
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_persistent_ws_codes(Pr
     __syncthreads();
     const int t = s_tile;
     if (t >= total_tiles) break;
-    const WsBlock k = block_of(a, locate_work(a, t, row_blocks));
+    const WsBlock k = wave_uniform(block_of(a, locate_work(a, t, row_blocks)));
     if (w < 4)
       ws_codes_range<true, CODE>(ws_args(a), k, L, w, lane);
     else

@@ -55,6 +55,37 @@ struct WsBlock {
   int kv_end;                 // cached rows of the request: none at or past it is read
 };
 
+// The block is the same for every lane; the compiler cannot always prove it
+// (fields read back from LDS or chosen per segment), and then it holds them
+// in vector registers that the core needs.  readfirstlane moves each field to
+// a scalar register.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ WsBlock wave_uniform(const WsBlock& k) {
+  WsBlock u;
+  u.q = wave_uniform(k.q);
+  u.out = wave_uniform(k.out);
+  u.lse = wave_uniform(k.lse);
+  u.lse_mul = __builtin_bit_cast(float, wave_uniform(__builtin_bit_cast(int, k.lse_mul)));
+  u.r0 = wave_uniform(k.r0);
+  u.nrows = wave_uniform(k.nrows);
+  u.vis0 = wave_uniform(k.vis0);
+  u.heads = wave_uniform(k.heads);
+  u.b = wave_uniform(k.b);
+  u.p_lo = wave_uniform(k.p_lo);
+  u.p_hi = wave_uniform(k.p_hi);
+  u.kv_end = wave_uniform(k.kv_end);
+  return u;
+}
+
 // A query row of a block: exists?, its index from the request's row 0, the
 // last cache row its token sees.
 struct QRow {
@@ -287,7 +318,7 @@ __device__ __forceinline__ bf16x4 softmax_half_sc(const f32x4& s, f32x4 sc, floa
   return p;
 }
 
-constexpr int kKAheadC = 3;
+constexpr int kKAheadC = 4;
 
 // One tile's codes in a value thread's registers (see above).
 constexpr int kCodeUnits = kI8RowBytes / 8 / 8;  // 9 units of 8 codes
