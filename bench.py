@@ -201,9 +201,11 @@ def time_calls(fn_list, stream, warmup: int, steps: int) -> float:
 # when the code of any of them changes; comments do not count).
 KERNEL_SOURCES = {
     "decode": ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_decode.hip",
-               "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h"],
+               "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h",
+               "mla_attention_paged_amd/csrc/mla_ws.h"],
     "prefill": ["mla_attention_paged_amd/csrc/mla_api.cpp", "mla_attention_paged_amd/csrc/mla_prefill.hip",
-                "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h"],
+                "mla_attention_paged_amd/csrc/mla_device.h", "mla_attention_paged_amd/csrc/mla_internal.h",
+                "mla_attention_paged_amd/csrc/mla_ws.h"],
 }
 # kernels whose counter readings make up one call of each leg
 LEG_KERNELS = {"decode": ("mla::decode_phase1_pipe", "mla::decode_merge"),

@@ -266,23 +266,23 @@ __device__ __forceinline__ void ws_store_rows(const WsBlock& k, const MLA_LDS fl
 
 // ---------------------------------------------------------------------------
 // INT8 / FP8 cache (CODE), K prefetch depth kKAheadC (the score waves here
-// also hold the row scales).  The value waves bring each tile's codes
-// straight into registers with ordinary global loads (value thread i: row
-// i / 8 of the tile, 72 consecutive code bytes; thread i < 32 also row i's
-// scale), a step ahead, and widen them to exact bf16 into one of three
-// converted tiles in LDS (the tile's 32 row scales beside it) while the score
-// waves compute.  No code byte passes through LDS.  Step k:
+// also hold the row scales).  Both wave kinds bring their share of each
+// tile's codes (see CodeRegs below; the value threads also the 32 row
+// scales) straight into registers with ordinary global loads, a step ahead,
+// and widen them to exact bf16 into one of three converted tiles in LDS (the
+// tile's 32 row scales beside it).  No code byte passes through LDS.  Step k:
 //  - B1(k): tile k is converted (in step k - 1);
 //  - score waves: softmax of tile k - 1 (probabilities times their row's
 //    scale, selected to 0 on masked rows so that a non-finite scale there
 //    cannot leak; the row sums take the unscaled probabilities), then the
 //    scores of tile k from its converted tile, each row's score times its
-//    scale; value waves: the conversion of tile k + 1 (its codes were
-//    requested in step k - 1) and the loads of tile k + 2's codes into the
-//    registers that just freed up;
+//    scale; value waves: the conversion of their part of tile k + 1 (its
+//    codes were requested in step k - 1) and the loads of their part of
+//    tile k + 2 into the registers that just freed up;
 //  - B2(k): the probabilities of tile k - 1 are published;
-//  - value waves: the value product of tile k - 1, re-reading each V
-//    fragment from tile k's converted tile behind its four MFMAs.
+//  - score waves: the same for their part of tiles k + 1 and k + 2; value
+//    waves: the value product of tile k - 1, re-reading each V fragment
+//    from tile k's converted tile behind its four MFMAs.
 // ---------------------------------------------------------------------------
 
 // mask_half with each tile row's scale (sc: rows 16kh + 4(lane>>4) + e).
@@ -320,39 +320,52 @@ __device__ __forceinline__ bf16x4 softmax_half_sc(const f32x4& s, f32x4 sc, floa
 
 constexpr int kKAheadC = 4;
 
-// One tile's codes in a value thread's registers (see above).
-constexpr int kCodeUnits = kI8RowBytes / 8 / 8;  // 9 units of 8 codes
+// Each tile row's 72 units of 8 codes are split between the two wave kinds:
+// value thread t (0..255) holds units kVUnits (t & 7) .. + kVUnits - 1 of tile
+// row t / 8 (and, for t < 32, row t's scale); score thread t holds units
+// 8 kVUnits + kSUnits (t & 7) .. + kSUnits - 1.  The value waves widen their
+// part in the score phase, the score waves theirs after B2, where they would
+// otherwise wait for the value product.
+constexpr int kCodeUnits = kI8RowBytes / 8 / 8;  // 9 units of 8 codes per thread and row
+constexpr int kVUnits = 6;
+constexpr int kSUnits = kCodeUnits - kVUnits;
 
+template <int N>
 struct CodeRegs {
-  u32x2 c[kCodeUnits];
+  u32x2 c[N];
   float sc;  // value threads 0 .. 31: row scale of tile row `thread`
 };
 
-// Request tile `half` (rows 32 half ..) of a page: rows at or past `rem` re-read
-// row 0's codes; their scales are read as they are and never used unmasked.
+// Request this thread's N units (from unit u0 + N (t & 7) of tile row t / 8)
+// of tile `half` (rows 32 half ..) of a page; rows at or past `rem` re-read
+// row 0's codes, and their scales are read as they are and never used
+// unmasked.  SCALE: also the row scale (threads t < 32).
+template <int N, bool SCALE>
 __device__ __forceinline__ void load_codes(const uint8_t* __restrict__ page, const float* __restrict__ spage,
-                                           int half, int rem, int vt, CodeRegs& r) {
-  const int t = vt >> 3;
-  const int row = kTileRows * half + t;
-  const uint8_t* src = page + (size_t)(row < rem ? row : 0) * kI8RowBytes + 8 * kCodeUnits * (vt & 7);
+                                           int half, int rem, int t, int u0, CodeRegs<N>& r) {
+  const int row = kTileRows * half + (t >> 3);
+  const uint8_t* src = page + (size_t)(row < rem ? row : 0) * kI8RowBytes + 8 * (u0 + N * (t & 7));
 #pragma unroll
-  for (int i = 0; i < kCodeUnits; ++i) r.c[i] = *reinterpret_cast<const u32x2*>(src + 8 * i);
-  r.sc = vt < kTileRows ? spage[kTileRows * half + vt] : 0.f;
+  for (int i = 0; i < N; ++i) r.c[i] = *reinterpret_cast<const u32x2*>(src + 8 * i);
+  if constexpr (SCALE) r.sc = t < kTileRows ? spage[kTileRows * half + t] : 0.f;
 }
 
-// Widen a tile's codes into a converted tile (pitch 1184, like a staged bf16
-// tile) and its scales into `tsc`.
-template <int CODE>
-__device__ __forceinline__ void store_codes(const CodeRegs& r, MLA_LDS uint8_t* cvt, MLA_LDS float* tsc, int vt) {
-  MLA_LDS uint8_t* dst = cvt + (vt >> 3) * kLdsPitch + 16 * kCodeUnits * (vt & 7);
+// Widen this thread's units into a converted tile (pitch 1184, like a staged
+// bf16 tile) and (SCALE) the row scales into `tsc`.
+template <int CODE, int N, bool SCALE>
+__device__ __forceinline__ void store_codes(const CodeRegs<N>& r, MLA_LDS uint8_t* cvt, MLA_LDS float* tsc, int t,
+                                            int u0) {
+  MLA_LDS uint8_t* dst = cvt + (t >> 3) * kLdsPitch + 16 * (u0 + N * (t & 7));
 #pragma unroll
-  for (int i = 0; i < kCodeUnits; ++i) {
+  for (int i = 0; i < N; ++i) {
     u32x4 o;
     o[0] = codepair_to_bf16<CODE, 0>(r.c[i][0]); o[1] = codepair_to_bf16<CODE, 1>(r.c[i][0]);
     o[2] = codepair_to_bf16<CODE, 0>(r.c[i][1]); o[3] = codepair_to_bf16<CODE, 1>(r.c[i][1]);
     *reinterpret_cast<MLA_LDS u32x4*>(dst + 16 * i) = o;
   }
-  if (vt < kTileRows) tsc[vt] = r.sc;
+  if constexpr (SCALE) {
+    if (t < kTileRows) tsc[t] = r.sc;
+  }
 }
 
 struct WsCodesLds {
@@ -392,7 +405,8 @@ __device__ __forceinline__ void ws_codes_range(const WsArgs& a, const WsBlock& k
   f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
   f32x4 o[kVQTiles][kVCTiles];
   bf16x4 vb[kVCTiles][2];
-  CodeRegs rc;  // value waves: the codes of the next tile to convert
+  CodeRegs<kVUnits> rc;  // value waves: their codes of the next tile to convert
+  CodeRegs<kSUnits> rs;  // score waves: theirs
   if (SCORE) {
     issue_q(x0.ok ? k_.q + (size_t)x0.qrow * kDqk : nullptr, lane, q0);
     issue_q(x1.ok ? k_.q + (size_t)x1.qrow * kDqk : nullptr, lane, q1);
@@ -457,57 +471,64 @@ __device__ __forceinline__ void ws_codes_range(const WsArgs& a, const WsBlock& k
     lds_barrier();
     const int ntiles = min(2 * n, (k_.kv_end - kPage * plo + kTileRows - 1) / kTileRows);
     auto lim_of = [&](const QRow& x, int k) { return x.ok ? x.vis_last - (kPage * plo + kTileRows * k) : -1; };
-    // tile k's codes (tiles past the window's last re-read the last one, so
-    // that the register sets always hold defined data; they are converted into
-    // a buffer nobody reads)
-    auto load = [&](int k, CodeRegs& r) {
-      if constexpr (!SCORE) {
-        const int kk = min(k, ntiles - 1);
-        const int p = kk >> 1;
-        const int pid = L.pid[p];
-        load_codes(a.kv + (size_t)pid * kI8PageBytes, a.kv_scale + (size_t)pid * kPage, kk & 1,
-                   k_.kv_end - kPage * (plo + p), vt, r);
-      }
+    // this thread's codes of tile k (tiles past the window's last re-read the
+    // last one, so that the registers always hold defined data; they are
+    // converted into a buffer nobody reads)
+    auto load = [&](int k) {
+      const int kk = min(k, ntiles - 1);
+      const int p = kk >> 1;
+      const int pid = L.pid[p];
+      const uint8_t* page = a.kv + (size_t)pid * kI8PageBytes;
+      const float* spage = a.kv_scale + (size_t)pid * kPage;
+      const int rem = k_.kv_end - kPage * (plo + p);
+      if constexpr (SCORE)
+        load_codes<kSUnits, false>(page, spage, kk & 1, rem, threadIdx.x, 8 * kVUnits, rs);
+      else
+        load_codes<kVUnits, true>(page, spage, kk & 1, rem, vt, 0, rc);
     };
-    auto convert = [&](int k, const CodeRegs& r) {
-      if constexpr (!SCORE) store_codes<CODE>(r, cvt_of(k), tsc_of(k), vt);
+    auto convert = [&](int k) {
+      if constexpr (SCORE)
+        store_codes<CODE, kSUnits, false>(rs, cvt_of(k), tsc_of(k), threadIdx.x, 8 * kVUnits);
+      else
+        store_codes<CODE, kVUnits, true>(rc, cvt_of(k), tsc_of(k), vt, 0);
     };
     auto value_step = [&](auto refill, int next) {
       value_product<decltype(refill)::value>(L.pb, L.al, vb, o, cvt_of(next), lane, vq);
     };
-    // steps k >= 1; `rn` holds the codes of tile k + 1
-    auto step = [&](int k, CodeRegs& rn) {
+    // steps k >= 1; the registers hold this thread's codes of tile k + 1
+    auto step = [&](int k) {
       lds_write_barrier();  // B1(k): tile k converted
       if (SCORE) {
         score_step(std::true_type{}, k, k - 1, lim_of(x0, k), lim_of(x1, k));
       } else {
-        convert(k + 1, rn);
-        load(k + 2, rn);
+        convert(k + 1);
+        load(k + 2);
       }
       lds_write_barrier();  // B2(k): the probabilities of tile k - 1 are published
       if (SCORE) {
         mx_mine[0] = mx0;
         mx_mine[64] = mx1;
+        convert(k + 1);
+        load(k + 2);
       } else {
         value_step(std::true_type{}, k);  // tile k - 1, then V of tile k into vb
       }
     };
 
-    load(0, rc);
-    convert(0, rc);
-    load(1, rc);
+    load(0);
+    convert(0);
+    load(1);
     lds_write_barrier();  // B1(0): tile 0 converted
     if (SCORE) score_tile(0, lim_of(x0, 0), lim_of(x1, 0));
     lds_write_barrier();  // B2(0)
     if (SCORE) {
       mx_mine[0] = mx0;
       mx_mine[64] = mx1;
-    } else {
-      convert(1, rc);
-      load(2, rc);
-      values_fetch(cvt_of(0), lane, vq, vb);  // V of tile 0
     }
-    for (int k = 1; k < ntiles; ++k) step(k, rc);
+    convert(1);
+    load(2);
+    if (!SCORE) values_fetch(cvt_of(0), lane, vq, vb);  // V of tile 0
+    for (int k = 1; k < ntiles; ++k) step(k);
     lds_write_barrier();  // B1'
     if (SCORE) score_step(std::false_type{}, -1, ntiles - 1, 0, 0);
     lds_write_barrier();  // B2'
