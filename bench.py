@@ -706,7 +706,7 @@ def main() -> int:
             del skv, sin, sws
             torch.cuda.empty_cache()
         result["scaled_cache_decode"] = {"workload": f"{case.name} with INT8 / FP8 (E4M3) rows and fp32 row scales",
-                                         "kernel": "mla_decode call (decode_phase1<scaled> + decode_merge)",
+                                         "kernel": "mla_decode call (decode_ws_codes<INT8 | FP8> + decode_merge)",
                                          "bound": "hbm", **legs}
 
     # ---------------- scaled caches: the prefill workload's shape with INT8 and FP8 rows ----------------
@@ -739,7 +739,7 @@ def main() -> int:
             torch.cuda.empty_cache()
         result["scaled_cache_prefill"] = {
             "workload": f"{base3.name} with INT8 / FP8 (E4M3) rows and fp32 row scales",
-            "kernel": "mla_prefill_varlen call (prefill_persistent_ws_codes: the value waves convert the next tile's codes)",
+            "kernel": "mla_prefill_varlen call (prefill_persistent_ws_codes: both wave kinds widen their share of the next tile's codes)",
             "bound": "mfma", **legs}
 
     # ---------------- append leg: the prefill workload's new rows into the cache ----------------
