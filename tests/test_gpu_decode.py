@@ -310,6 +310,19 @@ def test_decode_int8_needle():
     assert_close(out, lse, ref_out, ref_lse, "int8 needle")
 
 
+@pytest.mark.parametrize("kv_dtype", ["int8", "fp8"])
+@pytest.mark.parametrize("cus", [1, 2])
+def test_decode_codes_window_restart(cus, kv_dtype):
+    """INT8 / FP8 decode walks a share in windows of 256 staged page ids: 455 pages on
+    one or two workgroups cross a window edge inside a request (20,000 rows), switch
+    requests inside a window, and (one workgroup) write the final output directly."""
+    case = synth.make_decode_case(510, 3, 16, 4, seq_lens=[20000, 64, 9000], kv_dtype=kv_dtype)
+    with _cus(cus):
+        out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(out, lse, ref_out, ref_lse, f"{kv_dtype} cus {cus} window restart")
+
+
 # ---------------------------------------------------------------- FP8 (E4M3) cache
 
 FP8_SMALL = [
