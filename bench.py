@@ -337,7 +337,7 @@ def host_cpu_model() -> str:
 
 def oracle_threads() -> int:
     """Threads the oracle baseline runs with: the CPUs this process may use, at most 16
-    (a one-GPU machine's share of the host)."""
+    (the host CPU share that goes with one GPU of an eight-GPU node)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
