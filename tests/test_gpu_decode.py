@@ -106,6 +106,18 @@ def test_decode_ragged_many_requests():
     assert_close(out, lse, ref_out, ref_lse, "ragged 37")
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_decode_more_requests_than_the_length_cache(kv_dtype):
+    """600 requests: past the 512 lengths (and query offsets) the kernels cache in LDS, the
+    shares read the rest from memory; many requests per share, short and ragged lengths."""
+    g = np.random.default_rng(7)
+    lens = g.integers(1, 400, size=600)
+    case = synth.make_decode_case(211, 600, 16, 1, seq_lens=lens, max_seq_len=512, kv_dtype=kv_dtype)
+    out, lse = host(*run_decode(case))
+    ref_out, ref_lse = oracle.decode(case, nthreads=min(16, os.cpu_count() or 1))
+    assert_close(out, lse, ref_out, ref_lse, f"600 requests {kv_dtype}")
+
+
 @pytest.mark.parametrize("cus", [1, 5, 256])
 def test_decode_needle_bit_exact(cus):
     """q = 64 e_j and one row with value 32 at dim j: the needle's score leads every

@@ -84,3 +84,18 @@ def test_decode_varlen_no_tokens():
     case = _case(609, 16, [100, 50], [0, 0])
     out, lse = run_decode_varlen(case, max_q_len=2)   # enqueues nothing, must not fail
     torch.cuda.synchronize()
+
+
+def test_decode_varlen_more_requests_than_the_offset_cache():
+    """600 requests with 0-4 drafts each: query offsets past the 512 the kernels cache in
+    LDS come from memory; empty requests in between."""
+    g = np.random.default_rng(8)
+    q_lens = g.integers(0, 5, size=600)
+    seq_lens = q_lens + g.integers(0, 300, size=600)
+    seq_lens = np.maximum(seq_lens, 1)
+    case = _case(612, 16, seq_lens, q_lens)
+    out, lse = run_decode_varlen(case)
+    T = case.total_q()
+    ref_out, ref_lse = oracle.prefill(case, nthreads=min(16, os.cpu_count() or 1))
+    o, l_ = host(out, lse)
+    assert_close(o[:T], l_[:T], ref_out, ref_lse, "varlen 600 requests")

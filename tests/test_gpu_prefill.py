@@ -44,6 +44,19 @@ def test_prefill_ragged_batch():
     assert_close(out, lse, ref_out, ref_lse, "ragged 11")
 
 
+def test_prefill_many_requests():
+    """600 requests (the work list orders and sums them in one workgroup): prefixes of
+    0-300 rows, 0-6 new tokens each (empty requests included)."""
+    g = np.random.default_rng(9)
+    prefix = g.integers(0, 300, size=600)
+    new = g.integers(0, 7, size=600)
+    case = synth.make_prefill_case(421, 16, prefix_lens=prefix, new_lens=new)
+    out, lse = host(*run_prefill(case))
+    T = case.total_q()
+    ref_out, ref_lse = oracle.prefill(case, nthreads=min(16, os.cpu_count() or 1))
+    assert_close(out[:T], lse[:T], ref_out, ref_lse, "prefill 600 requests")
+
+
 def test_prefill_rows_equal_decode_rows_on_gpu():
     """Prefill token j of a request equals decode with q_len=1 on its first P+j+1 rows."""
     case = synth.make_prefill_case(411, 16, prefix_lens=[200], new_lens=[5])
