@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
-@pytest.mark.parametrize("page_size", [128, 256, 1536])
+@pytest.mark.parametrize("page_size", [128, 256, 1536, 4096])
 def test_decode_page_size_matches_oracle(page_size, kv_dtype):
     case = synth.make_decode_case(701, 3, 16, 4, seq_lens=[3100, 130, 2000], kv_dtype=kv_dtype,
                                   page_size=page_size)
@@ -36,7 +36,7 @@ def _as_64(cache):
     return synth.PagedCache(cache.kv_dtype, data, scale, pt64, cache.kv_lens, cache.poison_page * k, 64)
 
 
-@pytest.mark.parametrize("page_size", [128, 1536])
+@pytest.mark.parametrize("page_size", [128, 1536, 4096])
 def test_decode_page_size_bitwise_equals_64_view(page_size):
     a = synth.make_decode_case(702, 2, 16, 2, seq_lens=[4000, 777], page_size=page_size)
     b = synth.DecodeCase(a.batch, a.heads, a.q_len, a.q, _as_64(a.cache), a.max_seq_len, a.softmax_scale)
@@ -64,13 +64,14 @@ def test_decode_two_level_blocks():
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
-def test_prefill_page_size_matches_oracle(kv_dtype):
+@pytest.mark.parametrize("page_size", [1536, 4096])
+def test_prefill_page_size_matches_oracle(page_size, kv_dtype):
     case = synth.make_prefill_case(704, 16, prefix_lens=[1600, 0, 100], new_lens=[30, 70, 5], kv_dtype=kv_dtype,
-                                   page_size=1536)
+                                   page_size=page_size)
     out, lse = host(*run_prefill(case))
     ref_out, ref_lse = oracle.prefill(case)
     T = case.total_q()
-    assert_close(out[:T], lse[:T], ref_out, ref_lse, f"prefill page 1536 {kv_dtype}")
+    assert_close(out[:T], lse[:T], ref_out, ref_lse, f"prefill page {page_size} {kv_dtype}")
 
 
 def test_decode_varlen_page_size_matches_oracle():
