@@ -440,7 +440,10 @@ int mla_q_absorb(const void* q, const void* w_uk_t, void* q_out, int tokens, int
   g.rope_dst_row = g.c_row;
   g.rope_dst_head = g.c_head;
   g.rope_cols = MLA_DIM_ROPE;
-  const hipError_t e = launch_gemm(g, num_heads, static_cast<hipStream_t>(hip_stream));
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != MLA_OK) return rc;
+  const hipError_t e = launch_gemm(g, num_heads, cus, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -462,7 +465,10 @@ int mla_v_up(const void* o_lat, const void* w_uv, void* out, int tokens, int num
   g.m = tokens;
   g.n = MLA_DIM_VHEAD;
   g.k = MLA_DIM_V;
-  const hipError_t e = launch_gemm(g, num_heads, static_cast<hipStream_t>(hip_stream));
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != MLA_OK) return rc;
+  const hipError_t e = launch_gemm(g, num_heads, cus, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

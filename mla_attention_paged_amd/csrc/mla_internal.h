@@ -123,6 +123,6 @@ constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_prefill(const PrefillPlan& plan, const PrefillArgs& args, int kv_dtype, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& args, int kv_dtype, hipStream_t stream);
-hipError_t launch_gemm(const GemmArgs& g, int heads, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& g, int heads, int cus, hipStream_t stream);
 
 }  // namespace mla

@@ -61,8 +61,8 @@ hipError_t launch_append(const AppendArgs& a, int kv_dtype, hipStream_t) {
   if (a.total_new < 1 || (kv_dtype != 0) != (a.kv_scale != nullptr)) fail("append args");
   return hipSuccess;
 }
-hipError_t launch_gemm(const GemmArgs& g, int heads, hipStream_t) {
-  if (g.m < 1 || heads < 1 || !(g.n == 512 && g.k == 128) && !(g.n == 128 && g.k == 512)) fail("gemm args");
+hipError_t launch_gemm(const GemmArgs& g, int heads, int cus, hipStream_t) {
+  if (g.m < 1 || heads < 1 || cus < 1 || !(g.n == 512 && g.k == 128) && !(g.n == 128 && g.k == 512)) fail("gemm args");
   return hipSuccess;
 }
 hipError_t noalloc_scratch(void** p) {
