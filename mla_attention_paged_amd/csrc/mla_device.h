@@ -179,7 +179,12 @@ __device__ __forceinline__ int stage_src(int i, int lane, int half, int rem) {
 // not track it: its alias analysis cannot tell ring stages apart and would
 // otherwise wait for every in-flight stage before each LDS read.  The
 // kernels synchronise the ring themselves (wait_tile + s_barrier).  M0 holds
-// the LDS address; the s_nop covers the M0-write hazard.
+// the LDS address.  Wait states: a vector memory instruction that reads an
+// SGPR a VALU instruction wrote needs five (the compiler often writes the
+// base address with v_readfirstlane right before this block, and it does not
+// pad inline assembly for that hazard): the leading s_nop 2 gives three, the
+// M0 write and the s_nop 0 behind it (the M0-write hazard of an LDS load)
+// two more.
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, int voff, const MLA_LDS uint8_t* lds) {
   // Both scalar operands are wave-uniform; readfirstlane makes that explicit
   // so that they are allocated to SGPRs.
@@ -190,7 +195,7 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* base, int voff, const M
   const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t bs = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_nop 2\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(m), "v"(voff), "s"(bs)
                : "memory");
