@@ -224,6 +224,31 @@ def test_decode_nan_poison_has_no_effect():
     assert torch.isfinite(ob.float()).all()
 
 
+# (seed, seq_lens, cus): plans that take each merge kernel.  Workgroups per request
+# on average: 64 / 2 = 32 and 48 / 12 = 4 (the row-block merge, at most 40), 256 / 3
+# (the per-row merge); 12 requests of 1-2 pages on 48 workgroups leave shares empty.
+POISON_PLANS = [(311, [5000, 4000], 64), (312, [64, 65, 1, 128, 100, 3, 70, 127, 64, 2, 90, 33], 48),
+                (313, [3000, 2500, 700], 256)]
+
+
+@pytest.mark.parametrize("seed,lens,cus", POISON_PLANS, ids=["rows", "rows-sparse", "per-row"])
+def test_decode_merge_reads_only_written_partials(seed, lens, cus):
+    """The workspace starts as NaN bytes: both merge kernels read only the partials
+    phase one wrote (empty shares take weight 0 and a written slot), so the output
+    matches the oracle and is finite."""
+    case = synth.make_decode_case(seed, len(lens), 16, 1, seq_lens=lens)
+    d = decode_inputs(case)
+    nb = mla.mla_splitkv_workspace_size(case.batch, case.heads, case.q_len, case.total_q(), case.max_seq_len,
+                                        d["kind"])
+    ws = torch.full((max(nb, 1),), 255, dtype=torch.uint8, device="cuda")
+    with _cus(cus):
+        out, lse = run_decode(case, d, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    ref_out, ref_lse = oracle.decode(case)
+    assert_close(*host(out, lse), ref_out, ref_lse, f"seed {seed} cus {cus}")
+
+
 def test_decode_short_workspace_is_rejected():
     case = synth.make_decode_case(307, 4, 16, 4, seq_lens=[4096] * 4)
     ws = torch.empty(256, dtype=torch.uint8, device="cuda")
