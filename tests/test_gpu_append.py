@@ -69,6 +69,24 @@ def test_append_ragged_matches_oracle(kv_dtype):
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
+def test_append_many_requests_with_empty_ones(kv_dtype):
+    """150 requests (the row-to-request lookup reads 64 request offsets per round trip),
+    runs of empty requests among them, also at the 64-request boundaries."""
+    rng = np.random.default_rng(39)
+    batch, max_pages = 150, 2
+    num_pages = batch * max_pages
+    pt = rng.permutation(num_pages).reshape(batch, max_pages).astype(np.int32)
+    cache, scale = _fresh_cache(rng, kv_dtype, num_pages)
+    n = rng.integers(0, 4, size=batch).astype(np.int32)
+    n[[0, 5, 6, 7, 62, 63, 64, 65, 127, 128, 149]] = 0
+    n[[1, 66, 129]] = 9
+    start = rng.integers(0, max_pages * 64 - 9, size=batch).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    new = synth.bf16_bits(rng.standard_normal((int(cu[-1]), 576)).astype(np.float32))
+    _check(new, cu, start, cache, scale, kv_dtype, pt)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8", "fp8"])
 def test_append_edge_rows(kv_dtype):
     """Rows past the page table are dropped; zero rows, ties and huge / tiny magnitudes."""
     rng = np.random.default_rng(32)
@@ -167,6 +185,55 @@ def test_append_fp8_rounding_edges():
     assert np.array_equal(synth.bf16_to_f32(new)[0, :len(vals)], x[0, :len(vals)])   # exact inputs
     cu = np.array([0, 3], np.int32)
     _check(new, cu, np.array([5], np.int32), cache, scale, "fp8", pt)
+
+
+def _near_boundary_rows(kv_dtype, seed, n_scales=300):
+    """Rows of bf16 values whose fp32 quotient x / scale lies on or within 4 ulps of a
+    rounding boundary of the code (a half-integer for INT8, a midpoint between adjacent
+    E4M3 values for FP8), each row led by its max magnitude A so that its scale is
+    fp32(A / 127) or fp32(A / 448).  Power-of-two scales (A = 127 or 448) add exact
+    ties.  Returns (bf16 bits [rows, 576], number of near-boundary values)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    m = np.float32(127.0 if kv_dtype == "int8" else 448.0)
+    rng = np.random.default_rng(seed)
+    amaxes = list(rng.choice(vals[(vals > 0.01) & (vals < 1000)], n_scales, replace=False)) + [m, m * 2, m / 4]
+    rows, count = [], 0
+    for a in amaxes:
+        scale = np.float32(np.float32(a) / m)
+        x = vals[np.abs(vals) <= a]
+        q = np.abs((x / scale).astype(np.float32)).astype(np.float64)
+        ulp = np.spacing(q.astype(np.float32)).astype(np.float64)
+        if kv_dtype == "int8":
+            d = np.abs(q - np.floor(q) - 0.5)
+        else:
+            with np.errstate(divide="ignore"):
+                e = np.maximum(np.floor(np.log2(np.where(q > 0, q, 1.0))), -6)
+            grid = 2.0 ** (e - 3)
+            d = np.abs(q / grid - np.floor(q / grid) - 0.5) * grid
+        near = x[(d <= 4 * ulp) & (q > 0)][:575]
+        if len(near) == 0:
+            continue
+        row = np.zeros(576, np.float32)
+        row[0] = a
+        row[1:1 + len(near)] = near
+        rows.append(row)
+        count += len(near)
+    return synth.bf16_bits(np.stack(rows)), count
+
+
+@pytest.mark.parametrize("kv_dtype", ["int8", "fp8"])
+def test_append_codes_near_rounding_boundaries(kv_dtype):
+    """Quotients on or next to a rounding boundary of the code must round exactly as the
+    correctly rounded fp32 division x / scale does (ties to even)."""
+    new, count = _near_boundary_rows(kv_dtype, 36 if kv_dtype == "int8" else 37)
+    assert count > (1000 if kv_dtype == "int8" else 5000)
+    rows = new.shape[0]
+    pages = (rows + 63) // 64
+    pt = np.arange(pages, dtype=np.int32).reshape(1, pages)
+    cache, scale = _fresh_cache(np.random.default_rng(38), kv_dtype, pages)
+    _check(new, np.array([0, rows], np.int32), np.array([0], np.int32), cache, scale, kv_dtype, pt)
 
 
 def test_append_then_decode_fp8():
