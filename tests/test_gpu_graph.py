@@ -1,8 +1,7 @@
 """Decode, allocation-free decode, ragged decode, prefill and KV append captured into a
-HIP graph (torch.cuda.CUDAGraph) and replayed
-(GPU).  The calls allocate nothing, synchronise nothing and clear no memory with a
-memset, and their launch shapes depend only on host scalars, so a captured call is
-replayed as is.  Every replay, with eager calls and synchronisations between replays,
+HIP graph (torch.cuda.CUDAGraph) and replayed (GPU).  The calls allocate nothing,
+synchronise nothing and clear no memory with a memset, and their launch shapes depend
+only on host scalars, so a captured call is replayed as is.  Every replay, with eager calls and synchronisations between replays,
 must equal the eager result bit for bit."""
 import pytest
 import torch
