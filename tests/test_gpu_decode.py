@@ -434,6 +434,19 @@ def test_decode_workload2_sampled():
     print("workload2 sampled: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_decode_million_rows_sampled(kv_dtype):
+    """Contexts of 1,048,576 and 700,001 rows (2 drafts, 16 heads): about 100-150 shares per
+    request, so the merge reads its partials in several batches; the last draft of each
+    request is checked against the oracle."""
+    case = synth.make_decode_case(531, 2, 16, 2, seq_lens=[1 << 20, 700001], kv_dtype=kv_dtype)
+    out, lse = host(*run_decode(case))
+    toks = [1, 3]
+    ref_out, ref_lse = oracle.decode(case, tokens=toks, nthreads=min(16, os.cpu_count() or 1))
+    errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, f"1M rows {kv_dtype}")
+    print("million rows %s: max abs err %.3g, lse err %.3g, rel frob %.3g" % ((kv_dtype,) + errs))
+
+
 def test_decode_fp8_nan_code_tail_has_no_effect():
     """Rows past each request's end (and the poison page) hold the E4M3 NaN code 0x7F with a
     NaN scale: the output must equal the run with finite poison bit for bit."""
