@@ -183,3 +183,16 @@ def test_prefill_fp8_nan_code_tail_has_no_effect():
     torch.cuda.synchronize()
     assert np.array_equal(bits(oa), bits(ob)) and torch.equal(la, lb)
     assert torch.isfinite(ob.float()).all()
+
+
+def test_prefill_million_row_prefix_sampled():
+    """One request with a 1,048,571-row cached prefix (64 windows of staged page ids, a
+    ragged last page) and 1,500 new tokens, beside a short one.  The oracle checks the long
+    request's first and last new token and the short one's last, all heads: the first and
+    last work tiles of the long request walk every window."""
+    case = synth.make_prefill_case(532, 16, prefix_lens=[(1 << 20) - 5, 300], new_lens=[1500, 37])
+    out, lse = host(*run_prefill(case))
+    toks = [0, 1499, 1536]
+    ref_out, ref_lse = oracle.prefill(case, tokens=toks, nthreads=NT)
+    errs = assert_close(out[toks], lse[toks], ref_out, ref_lse, "1M prefix")
+    print("million-row prefix: max abs err %.3g, lse err %.3g, rel frob %.3g" % errs)
