@@ -29,7 +29,9 @@ The other decode workloads (``configs``: the 256-row latency case, the
 ragged 16-request batch with 32 heads, the 256K-row INT8 batch) are timed
 the same way, each after a fixed warm-up of its own (0.25 s of its calls,
 whatever --warmup says), with two or three cache copies rotated (the
-256-row case is deliberately cache-hot).
+256-row case is deliberately cache-hot).  Beside them: 128 folded rows on the 64K
+cache (``wide_rows_decode``) and a serving batch of 64 requests of 4K rows
+(``batch_decode``).
 
 The CPU baseline is the fp64 oracle on the host's cores (at most 16
 threads), timed on the full decode workload (all 16 query tokens, all
@@ -582,6 +584,11 @@ def main() -> int:
         wcase = synth.make_decode_case(2, 4, 32, 4, seq_lens=[65536] * 4, name="decode_b4_h32_q4_L64K")
         result["wide_rows_decode"] = decode_leg(mla, torch, stream, wcase, 3, 100, 0.25)
         del wcase
+        # a serving batch: 64 requests of 4K rows, 4 drafts (4 phase-one workgroups per
+        # request, so the partials are merged by row blocks)
+        bcase = synth.make_decode_case(11, 64, 16, 4, seq_lens=[4096] * 64, name="decode_b64_h16_q4_L4K")
+        result["batch_decode"] = decode_leg(mla, torch, stream, bcase, 3, 100, 0.25)
+        del bcase
 
     # ---------------- absorption and up-projection on the prefill workload's tokens ----------------
     if not args.no_absorb:
