@@ -460,10 +460,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_ws_codes(DecodeArgs a) 
     if (k.r0 >= k.nrows) continue;  // this row block has no rows of the request
     __syncthreads();                // the previous segment is done with the LDS
     const WsBlock ku = wave_uniform(k);
+    constexpr int kAhead = CODE == kCodeInt8 ? kKAheadDecodeInt8 : kKAheadC;
     if (w < 4)
-      ws_codes_range<true, CODE>(wa, ku, L, w, lane);
+      ws_codes_range<true, CODE, kAhead>(wa, ku, L, w, lane);
     else
-      ws_codes_range<false, CODE>(wa, ku, L, w, lane);
+      ws_codes_range<false, CODE, kAhead>(wa, ku, L, w, lane);
   }
 }
 

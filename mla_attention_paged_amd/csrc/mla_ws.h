@@ -265,7 +265,7 @@ __device__ __forceinline__ void ws_store_rows(const WsBlock& k, const MLA_LDS fl
 }
 
 // ---------------------------------------------------------------------------
-// INT8 / FP8 cache (CODE), K prefetch depth kKAheadC (the score waves here
+// INT8 / FP8 cache (CODE), K prefetch depth KAHEAD (the score waves here
 // also hold the row scales).  Both wave kinds bring their share of each
 // tile's codes (see CodeRegs below; the value threads also the 32 row
 // scales) straight into registers with ordinary global loads, a step ahead,
@@ -318,7 +318,12 @@ __device__ __forceinline__ bf16x4 softmax_half_sc(const f32x4& s, f32x4 sc, floa
   return p;
 }
 
+// K fragments the score waves read ahead of their MFMAs: 4 measured best on
+// the INT8 and FP8 prefill and the FP8 decode, 3 on the INT8 decode (67.7
+// against 69.6 us on the 4 x 64K shape, 399 against 403 us on 8 x 256K; 3 costs
+// the FP8 prefill 8%, and 5 or 6 were slower everywhere).
 constexpr int kKAheadC = 4;
+constexpr int kKAheadDecodeInt8 = 3;
 
 // Each tile row's 72 units of 8 codes are split between the two wave kinds:
 // value thread t (0..255) holds units kVUnits (t & 7) .. + kVUnits - 1 of tile
@@ -380,7 +385,7 @@ struct WsCodesLds {
 // One block of up to 64 query rows against sub-pages [p_lo, p_hi) of its
 // request, INT8 / FP8 cache (see above), as a score wave (SCORE) or a value
 // wave: both kinds pass the same barriers in the same order.
-template <bool SCORE, int CODE>
+template <bool SCORE, int CODE, int KAHEAD = kKAheadC>
 __device__ __forceinline__ void ws_codes_range(const WsArgs& a, const WsBlock& k_, const WsCodesLds& L, int w,
                                                int lane) {
   const int rg = (w & 3) >> 1;  // score waves: row group
@@ -428,10 +433,10 @@ __device__ __forceinline__ void ws_codes_range(const WsArgs& a, const WsBlock& k
   auto score_step = [&](auto with_scores, int kk, int kprev, int lim0, int lim1) {
     constexpr bool kScores = decltype(with_scores)::value;
     const MLA_LDS uint8_t* kbase = cvt_of(kk < 0 ? 0 : kk) + tile_off(16 * hh + (lane & 15), g);
-    bf16x8 kb[kKAheadC];
+    bf16x8 kb[KAHEAD];
     if constexpr (kScores) {
 #pragma unroll
-      for (int d = 0; d < kKAheadC; ++d) kb[d] = lds_b128(kbase + 64 * d);
+      for (int d = 0; d < KAHEAD; ++d) kb[d] = lds_b128(kbase + 64 * d);
     }
     __builtin_amdgcn_sched_barrier(0);  // the first K reads go out before the softmax
     const f32x4 scp = tsc4(kprev);
@@ -446,8 +451,8 @@ __device__ __forceinline__ void ws_codes_range(const WsArgs& a, const WsBlock& k
       f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
 #pragma unroll
       for (int ks = 0; ks < kQFrags; ++ks) {
-        const bf16x8 kf = kb[ks % kKAheadC];
-        if (ks + kKAheadC < kQFrags) kb[ks % kKAheadC] = lds_b128(kbase + 64 * (ks + kKAheadC));
+        const bf16x8 kf = kb[ks % KAHEAD];
+        if (ks + KAHEAD < kQFrags) kb[ks % KAHEAD] = lds_b128(kbase + 64 * (ks + KAHEAD));
         if (ks & 1) {
           a1 = mfma16x16x32(kf, q0[ks], a1);
           b1 = mfma16x16x32(kf, q1[ks], b1);
