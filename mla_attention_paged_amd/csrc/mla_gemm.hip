@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256, 2) void nt_gemm(GemmArgs g, int blocks_per_wg)
       const int last = g.m - 1 - m0;
       MLA_LDS uint8_t* const dst = (MLA_LDS uint8_t*)tile;
 #pragma unroll
-      for (int r = w; r < ROWS; r += 4) {  // wave load r: row r, lane l: chunk l ^ (r & 15)
+      for (int i = 0; i < ROWS / 4; ++i) {  // wave load r: row r, lane l: chunk l ^ (r & 15)
+        const int r = w + 4 * i;
         const uint16_t* src = A + (size_t)(m0 + (r < last ? r : last)) * g.a_row;
         lds_dma16(reinterpret_cast<const uint8_t*>(src), 16 * (lane ^ (r & 15)), dst + r * 1024);
       }
@@ -129,8 +130,10 @@ __global__ __launch_bounds__(256, 2) void nt_gemm(GemmArgs g, int blocks_per_wg)
     __syncthreads();
     // whole rows: N / 8 chunks of 16 bytes per token
     constexpr int OCPR = N / 8;
+    static_assert(ROWS * OCPR % 256 == 0, "whole store rounds");
 #pragma unroll
-    for (int c = threadIdx.x; c < ROWS * OCPR; c += 256) {
+    for (int it = 0; it < ROWS * OCPR / 256; ++it) {
+      const int c = threadIdx.x + 256 * it;
       const int r = c / OCPR, q = c - r * OCPR;
       if (m0 + r < g.m)
         *reinterpret_cast<u32x4*>(C + (size_t)(m0 + r) * g.c_row + 8 * q) =
