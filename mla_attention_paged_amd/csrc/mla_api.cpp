@@ -281,6 +281,9 @@ int decode_impl(const void* q, const int32_t* cu_q, const void* kv_cache, const 
   a.heads = num_heads;
   a.rows = q_len * num_heads;
   a.grid = plan.grid;
+  // the bf16 decode's first tile is requested before the lengths arrive, on the
+  // guess that every request holds max_seq_len rows (uniform query counts only)
+  a.guess_pages = cu_q ? 0 : (max_seq_len + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
   a.scale_log2 = softmax_scale * kLog2e;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;

@@ -158,13 +158,20 @@ __device__ __forceinline__ ReqQ req_q(const DecodeArgs& a, const int* s_tok, int
   return {t0, a.cu_q[b + 1] - t0};
 }
 
+// A share of the page stream: pages lo .. hi - 1, starting at page j0 of
+// request b0 (b0 = batch when the share is empty).
+struct Share {
+  int lo, hi, b0, j0;
+};
+
 // Wave 0 of workgroup g locates its share floor(g*P/G) .. floor((g+1)*P/G)
-// of the page stream and the (request, page) where it starts, and fills the
-// length cache (and, for per-request query counts, the token-offset cache,
-// entries 0 .. min(batch, kLenCache)); workgroup (0, 0) also records the
-// page prefix sums for the merge.
-__device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lane, int* s_info, int* s_len,
-                                             int* s_tok) {
+// of the page stream and the (request, page) where it starts (returned, and
+// stored in s_info[0..3] for the other waves), and fills the length cache
+// (and, for per-request query counts, the token-offset cache, entries 0 ..
+// min(batch, kLenCache)); workgroup (0, 0) also records the page prefix sums
+// for the merge.
+__device__ __forceinline__ Share locate_share(const DecodeArgs& a, int g, int lane, int* s_info, int* s_len,
+                                              int* s_tok) {
   if (a.cu_q)
     for (int b = lane; b <= a.batch && b <= kLenCache; b += 64) s_tok[b] = a.cu_q[b];
   const int G = a.grid;
@@ -180,7 +187,7 @@ __device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lan
     P += __shfl(incl, 63);
   }
   if (write_cum && lane == 0) a.cum_pages[a.batch] = (int)P;
-  const Lens lens{a, s_len};  // this wave's own LDS writes are visible to its later reads
+  const Lens lens{a, s_len};  // lane b reads back the entry it wrote
   const long long lo = P * g / G, hi = P * (g + 1) / G;
   int b0 = a.batch, j0 = 0;
   if (lo < hi) {
@@ -207,18 +214,23 @@ __device__ __forceinline__ void locate_share(const DecodeArgs& a, int g, int lan
     s_info[2] = b0;
     s_info[3] = j0;
   }
+  return {(int)lo, (int)hi, b0, j0};
 }
 
-// Fill the window's tile list: the valid tiles (half pages holding at least
-// one of their request's rows) of pages wlo .. wlo + n - 1 of the stream,
-// starting at request cb, page cj, in stream order.  Tile t: page s_pid[t],
+// Orders this wave's earlier LDS writes before its later LDS reads of the
+// same locations by other lanes.  The hardware performs a wave's LDS
+// accesses in order; without a fence the compiler may still move a read of
+// another lane's entry above the write (no barrier separates them).
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// A window's tile list (one wave builds it): the valid tiles (half pages
+// holding at least one of their request's rows) of the n pages of the stream
+// from request cb, page cj on, in stream order.  Tile t: page s_pid[t],
 // request s_req[t] >> 1, half s_req[t] & 1, s_rem[t] = the request's rows
-// from the tile's first row (> 0).  Wave 0 builds the list; every thread
-// advances the cursor past the n pages.  Returns the tile count through
-// s_info[0].
-__device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, const Lens& lens, int n, int& cb, int& cj,
-                                                  int* s_pid, int* s_req, int* s_rem, int* s_count, int w, int lane) {
-  if (w == 0) {
+// from the tile's first row (> 0).  The tile count goes to *s_count.
+__device__ __forceinline__ void window_tiles(const DecodeArgs& a, const Lens& lens, int n, int cb, int cj,
+                                             int* s_pid, int* s_req, int* s_rem, int* s_count, int lane) {
+  {
     int base = 0;
     for (int k0 = 0; k0 < n; k0 += 64) {
       const int k = k0 + lane;
@@ -252,7 +264,12 @@ __device__ __forceinline__ void fill_window_tiles(const DecodeArgs& a, const Len
     }
     if (lane == 0) *s_count = base;
   }
-  int b = cb, off = cj + n;  // advance the cursor by n pages (uniform across the workgroup)
+}
+
+// Move the cursor (request cb, page cj) past n pages of the stream (every
+// thread, with the same result).
+__device__ __forceinline__ void advance_cursor(const DecodeArgs& a, const Lens& lens, int n, int& cb, int& cj) {
+  int b = cb, off = cj + n;
   for (;;) {
     const int np = (lens(b) + kPage - 1) / kPage;
     if (off < np || b + 1 >= a.batch) break;
@@ -286,11 +303,48 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = blockIdx.x;
-  if (w == 0) locate_share(a, g, lane, s_info, s_len, s_tok);
+  auto stage = [&](int t) { return ring + (t % kPStages) * kStageBytes; };
+
+  // Guessed start.  The share, its first tile and its query block wait on
+  // two dependent loads (the lengths, then the page table).  If every
+  // request held max_seq_len rows, share g would start at page jg of request
+  // bg.  While wave 0 locates the share, waves 1-7 load bg's length and page
+  // jg's table entry, request that page's first tile if the page exists, and
+  // stage bg's query block.  When the located share starts at page jg of
+  // request bg (so the page exists), both are already on their way;
+  // otherwise the waves drain them and the normal start follows.
+  int bg = -1, jg = 0;
+  if (a.guess_pages > 0) {
+    const long long Pg = (long long)a.batch * a.guess_pages;
+    const long long lo = Pg * g / a.grid;
+    if (lo < Pg * (g + 1) / a.grid) {
+      bg = (int)(lo / a.guess_pages);
+      jg = (int)(lo - (long long)bg * a.guess_pages);
+    }
+  }
+  if (w == 0) {
+    const Share sh = locate_share(a, g, lane, s_info, s_len, s_tok);
+    // the first window's tile list, while waves 1-7 issue their loads (its
+    // length lookups read the cache entries other lanes just wrote)
+    wave_lds_fence();
+    if (sh.lo < sh.hi)
+      window_tiles(a, Lens{a, s_len}, min(kWin, sh.hi - sh.lo), sh.b0, sh.j0, s_pid, s_req, s_rem, &s_info[4], lane);
+  } else if (bg >= 0) {
+    const int len_g = clamp_len(a.seq_lens[bg], a.max_pages);
+    const int pid_g = sub_page(a.page_table, (size_t)bg * a.pt_stride, jg, a.sub);
+    if (jg < (len_g + kPage - 1) / kPage)
+      stage_tile<kWaves - 1>(a.kv + (size_t)pid_g * kPageBytes, 0, len_g - kPage * jg, stage(0), w - 1, lane);
+    const int nrows = min(a.rows - kBlockRows * (int)blockIdx.y, kBlockRows);
+    if (nrows > 0)
+      stage_q(a.q + ((size_t)bg * a.rows + kBlockRows * blockIdx.y) * kDqk, nrows, stage(1), w - 1, kWaves - 1,
+              lane);
+  }
   __syncthreads();
   const Lens lens{a, s_len};
   const int seg_lo = s_info[0], seg_hi = s_info[1];
-  if (seg_lo >= seg_hi) return;  // empty share (more workgroups than pages)
+  const bool guessed = bg >= 0 && s_info[2] == bg && s_info[3] == jg && seg_lo < seg_hi;
+  if (!guessed) wait_vmcnt<0>();  // no guessed load may land after the stages are reused
+  if (seg_lo >= seg_hi) return;   // empty share (more workgroups than pages)
   int cb = s_info[2], cj = s_info[3];
 
   const int half = w >> 2;
@@ -308,7 +362,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   };
   MLA_LDS f32x4* const xmine = xchg + 64 * w + lane;
   MLA_LDS f32x4* const xpart = xchg + 64 * (w ^ 4) + lane;
-  auto stage = [&](int t) { return ring + (t % kPStages) * kStageBytes; };
 
   RowState st;
   bf16x8 qf[kQFrags];
@@ -322,7 +375,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   // the first tile's delay that tile by about 2 us.)
   const int q_b = cb;  // request whose query block is staged
   bool q_staged = true;
-  if (w > 0) {
+  if (w > 0 && !guessed) {
     const ReqQ r = req_q(a, s_tok, q_b);
     const int nrows = min(r.n * a.heads - kBlockRows * (int)blockIdx.y, kBlockRows);
     if (nrows > 0)
@@ -332,19 +385,31 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
 
   for (int wlo = seg_lo; wlo < seg_hi; wlo += kWin) {
     const int n = min(kWin, seg_hi - wlo);
-    __syncthreads();  // the previous window's list and stages are no longer read
-    fill_window_tiles(a, lens, n, cb, cj, s_pid, s_req, s_rem, &s_info[4], w, lane);
-    __syncthreads();
+    if (wlo != seg_lo) {  // the first window's list was built before the first barrier
+      __syncthreads();    // the previous window's list and stages are no longer read
+      if (w == 0) window_tiles(a, lens, n, cb, cj, s_pid, s_req, s_rem, &s_info[4], lane);
+      __syncthreads();
+    }
+    advance_cursor(a, lens, n, cb, cj);
     const int N = s_info[4];
     auto issue = [&](int t) {
       stage_tile<kWaves>(a.kv + (size_t)s_pid[t] * kPageBytes, s_req[t] & 1, s_rem[t] + kTileRows * (s_req[t] & 1),
                          stage(t), w, lane);
     };
-    issue(0);
+    if (!guessed || wlo != seg_lo) issue(0);
     for (int t0 = 0; t0 < N;) {
       const int b = s_req[t0] >> 1;
-      int t1 = t0 + 1;
-      while (t1 < N && (s_req[t1] >> 1) == b) ++t1;
+      // the segment ends at the first later tile of another request: a
+      // wave-wide compare of 64 list entries at a time (one entry per step
+      // would put an LDS round trip per tile in front of the first tile)
+      int t1 = N;
+      for (int base = t0 + 1; base < N; base += 64) {
+        const unsigned long long m = __ballot(base + lane < N && (s_req[base + lane] >> 1) != b);
+        if (m) {
+          t1 = base + __ffsll((long long)m) - 1;
+          break;
+        }
+      }
       if (wave_rows && b != cur_b) {
         if (cur_b >= 0) flush_rows(a, st, tok0, g + cur_b, row, row_ok, half, lane);
         set_req(b);

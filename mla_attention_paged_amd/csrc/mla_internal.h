@@ -30,6 +30,7 @@ struct DecodeArgs {
   int heads;
   int rows;                   // q_len * heads: folded query rows of one request (with cu_q: at most)
   int grid;                   // phase-one workgroups
+  int guess_pages;            // 64-row sub-pages of a request of max_seq_len rows (0: no guessed start)
   float scale_log2;           // softmax_scale * log2(e)
   uint16_t* out;              // bf16 [batch * rows, 512]
   float* lse;                 // fp32 [batch * rows]
