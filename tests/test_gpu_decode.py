@@ -224,6 +224,31 @@ def test_decode_nan_poison_has_no_effect():
     assert torch.isfinite(ob.float()).all()
 
 
+# The bf16 decode requests its first tile and query block before the lengths arrive,
+# guessing that every request holds max_seq_len rows.  (seed, seq_lens, max_seq_len,
+# cus): the guess right for every workgroup; wrong for every one (each request shorter,
+# so most guessed pages lie past the lengths); right for the full-length requests only;
+# more workgroups than pages (guessed tiles issued by workgroups whose share is empty).
+GUESS_CASES = [(321, [2048] * 4, 2048, 64), (322, [700] * 4, 2048, 64),
+               (323, [2048, 300, 2048, 1100], 2048, 48), (324, [64, 64], 2048, 256)]
+
+
+@pytest.mark.parametrize("seed,lens,max_len,cus", GUESS_CASES, ids=["right", "wrong", "mixed", "idle"])
+def test_decode_guessed_start(seed, lens, max_len, cus):
+    """Parity with the oracle, and NaN rows in every page past the lengths (where the
+    unused page-table entries point) leave the output bitwise unchanged."""
+    a = synth.make_decode_case(seed, len(lens), 16, 4, seq_lens=lens, max_seq_len=max_len)
+    b = synth.make_decode_case(seed, len(lens), 16, 4, seq_lens=lens, max_seq_len=max_len,
+                               poison=synth.POISON_NAN)
+    with _cus(cus):
+        oa, la = run_decode(a)
+        ob, lb = run_decode(b)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode(a)
+    assert_close(*host(oa, la), ref_out, ref_lse, f"seed {seed}")
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)) and torch.equal(la, lb)
+
+
 # (seed, seq_lens, cus): plans that take each merge kernel.  Workgroups per request
 # on average: 64 / 2 = 32 and 48 / 12 = 4 (the row-block merge, at most 40), 256 / 3
 # (the per-row merge); 12 requests of 1-2 pages on 48 workgroups leave shares empty.
