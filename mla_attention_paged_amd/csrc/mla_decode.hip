@@ -313,8 +313,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   // stage bg's query block.  When the located share starts at page jg of
   // request bg (so the page exists), both are already on their way;
   // otherwise the waves drain them and the normal start follows.
+  // (the test of the query pointer, never null here, makes it load with the first
+  // arguments, before the guessed loads go out: a later first use would wait for every
+  // outstanding scalar load, theirs included)
   int bg = -1, jg = 0;
-  if (a.guess_pages > 0) {
+  if (a.guess_pages > 0 && a.q != nullptr) {
     const long long Pg = (long long)a.batch * a.guess_pages;
     const long long lo = Pg * g / a.grid;
     if (lo < Pg * (g + 1) / a.grid) {
@@ -332,12 +335,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   } else if (bg >= 0) {
     const int len_g = clamp_len(a.seq_lens[bg], a.max_pages);
     const int pid_g = sub_page(a.page_table, (size_t)bg * a.pt_stride, jg, a.sub);
-    if (jg < (len_g + kPage - 1) / kPage)
-      stage_tile<kWaves - 1>(a.kv + (size_t)pid_g * kPageBytes, 0, len_g - kPage * jg, stage(0), w - 1, lane);
     const int nrows = min(a.rows - kBlockRows * (int)blockIdx.y, kBlockRows);
     if (nrows > 0)
       stage_q(a.q + ((size_t)bg * a.rows + kBlockRows * blockIdx.y) * kDqk, nrows, stage(1), w - 1, kWaves - 1,
               lane);
+    if (jg < (len_g + kPage - 1) / kPage)
+      stage_tile<kWaves - 1>(a.kv + (size_t)pid_g * kPageBytes, 0, len_g - kPage * jg, stage(0), w - 1, lane);
   }
   __syncthreads();
   const Lens lens{a, s_len};
