@@ -309,13 +309,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_phase1_pipe(DecodeArgs 
   // two dependent loads (the lengths, then the page table).  If every
   // request held max_seq_len rows, share g would start at page jg of request
   // bg.  While wave 0 locates the share, waves 1-7 load bg's length and page
-  // jg's table entry, request that page's first tile if the page exists, and
-  // stage bg's query block.  When the located share starts at page jg of
-  // request bg (so the page exists), both are already on their way;
-  // otherwise the waves drain them and the normal start follows.
-  // (the test of the query pointer, never null here, makes it load with the first
-  // arguments, before the guessed loads go out: a later first use would wait for every
-  // outstanding scalar load, theirs included)
+  // jg's table entry, stage bg's query block while those loads are out, and
+  // then request page jg's first tile if the page exists.  When the located
+  // share starts at page jg of request bg (so the page exists), both are
+  // already on their way; otherwise the waves drain them and the normal start
+  // follows.  The test of the query pointer (never null here) makes it load
+  // with the first arguments, before the guessed loads go out: a later first
+  // use would wait for every outstanding scalar load, theirs included.
   int bg = -1, jg = 0;
   if (a.guess_pages > 0 && a.q != nullptr) {
     const long long Pg = (long long)a.batch * a.guess_pages;
