@@ -153,7 +153,11 @@ int mla_splitkv_workspace_size(int batch, int num_heads, int max_q_len, int tota
  *   seq_lens   int32 [batch] on the device: cached rows of request b,
  *              the q_len new tokens included
  *   max_seq_len  host upper bound of seq_lens; max_pages_per_req must be
- *              at least ceil(max_seq_len / page_size)
+ *              at least ceil(max_seq_len / page_size).  The bf16 kernel also
+ *              requests each workgroup's first tile before the lengths
+ *              arrive, guessing that every request holds max_seq_len rows;
+ *              the guess is checked, so any lengths give the same result,
+ *              and batches whose lengths all equal max_seq_len start soonest
  *   softmax_scale  multiplies <q, row> (for example 1/sqrt(192))
  *   out, lse   outputs, [batch * q_len, num_heads, 512] bf16 and
  *              [batch * q_len, num_heads] fp32
